@@ -1,0 +1,231 @@
+"""Benchmark of the sparse layer's decode/verify step on one MI355X.
+
+One step = indexer score + top-512 block select (sa_indexer_topk) followed by
+block-sparse GQA attention over the selected + current blocks (sa_sparse_decode,
+which merges partitions itself when it splits), for one batch of the 128K-context
+MTP verify workload: 64 sequences with lengths uniform in [98304, 131072], the
+last 4 positions of each as query tokens (256 tokens), bf16 paged KV with
+randomly permuted 64-token pages, integer index inputs in [-4, 4], Q/K/V ~ N(0,1).
+Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. `value` is query tokens per second of the whole step.
+The roofline object covers the dominant kernel (the attention kernel): its
+algorithmic bytes (distinct K/V blocks read + Q + O + selection + lse) divided by
+its mean duration measured with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn decode query-tokens/s at 128K ctx, batch 64; achieved HBM GB/s"
+PEAK_HBM_GBPS = 8000.0
+SCALE = 1.0 / math.sqrt(192.0)
+PMC_FILE = os.path.join(ROOT, "profiles", "attention_mtp_verify_128k_pmc.json")
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_block_indexed_amd", "csrc", "sa_attention.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None if they are missing or were taken on a different kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, sel_host, budget_s: float = 20.0, max_tokens: int = 64):
+    """The fp64 oracle timed on this host over a bounded sample of the same
+    workload: whole sequences' verify tokens, until the budget is spent."""
+    import torch
+    from oracle import sa_oracle as O
+    from sparse_block_indexed_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    done, t_cpu = 0, 0.0
+    seqs_done = 0
+    for b in range(wl.batch):
+        toks = [t for t in range(wl.n_tok) if int(wl.q_seq[t]) == b]
+        row = wl.page_table[b]
+        # host copies of what the oracle reads (not timed): the sequence's index
+        # keys and the pages of every attended block
+        max_cb = max(int(wl.q_pos[t]) // 8 for t in toks)
+        npg = (max_cb + 7) // 8
+        dev = wl.k_idx_cache.device
+        kidx = I.bf16_bits(wl.k_idx_cache.index_select(0, torch.as_tensor(row[:npg].astype(np.int64), device=dev)))
+        pages = set()
+        for t in toks:
+            p = int(wl.q_pos[t])
+            pages |= {int(x) // 8 for x in sel_host[t] if x >= 0} | {p // 64}
+        logical = np.array(sorted(pages), dtype=np.int64)
+        idx = torch.as_tensor(row[logical].astype(np.int64), device=dev)
+        kc, vc = I.bf16_bits(wl.k_cache.index_select(0, idx)), I.bf16_bits(wl.v_cache.index_select(0, idx))
+        compact = np.full(row.shape[0], -1, dtype=np.int64)
+        compact[logical] = np.arange(len(logical))
+        qb = [I.bf16_bits(wl.q[t]) for t in toks]
+        qib = [I.bf16_bits(wl.q_idx[t]) for t in toks]
+        t0 = time.perf_counter()
+        for j, t in enumerate(toks):
+            p = int(wl.q_pos[t])
+            keys = O.index_keys(kidx, np.arange(npg), p // 8)
+            sel = O.indexer_topk_token(O.bf16_to_f64(qib[j]), keys, 512)
+            O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.sparse_token_positions(sel, p), SCALE)
+        t_cpu += time.perf_counter() - t0
+        done += len(toks)
+        seqs_done += 1
+        if t_cpu >= budget_s or done >= max_tokens:
+            break
+    return {"value": done / t_cpu, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} verify tokens ({seqs_done} sequences) of the 128K batch, fp64 numpy oracle, "
+                      f"{t_cpu:.1f} s of CPU time, host copies excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps, each after a 1 GiB write that evicts L2/MALL (reported separately)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (see the sharding notes in "
+              "DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return
+
+    from sparse_block_indexed_amd import bytes_model as B
+    from sparse_block_indexed_amd import inputs as I
+    from sparse_block_indexed_amd import ops
+
+    ops.load_library()
+    wl = I.config_workload(1, device=dev)
+    pt, sl, qs, qp = wl.device_ints(dev)
+    topk = 512
+    n_tok = wl.n_tok
+    S = ops.resolve_num_splits(n_tok, topk + 1, 0)
+    sel = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk), dtype=torch.uint8, device=dev)
+    out = torch.empty((n_tok, 64, 192), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((n_tok, 64), dtype=torch.float32, device=dev)
+    part_o = torch.empty((n_tok, S, 64, 192), dtype=torch.float32, device=dev) if S > 1 else None
+    part_lse = torch.empty((n_tok, S, 64), dtype=torch.float32, device=dev) if S > 1 else None
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=0, out=out,
+                          out_lse=lse, part_o=part_o, part_lse=part_lse)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+
+    # cold-cache steps: a 1 GiB write between steps evicts L2 and the 256 MB MALL
+    cold_ms = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold = []
+        for _ in range(args.cold_steps):
+            flush.fill_(1.0)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(ev)
+            torch.cuda.synchronize()
+            cold.append((ev[0].elapsed_time(ev[2]), ev[1].elapsed_time(ev[2])))
+        cold_ms = float(np.mean([c[0] for c in cold]))
+        cold_attn_ms = float(np.mean([c[1] for c in cold]))
+        del flush
+
+    sel_host = sel.cpu().numpy()
+    attn_bytes = B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host)
+    idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk)
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = counter_traffic()
+    result = {
+        "metric": METRIC,
+        "value": n_tok / (ms_per_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mtp_verify_128k_b64", "batch": wl.batch, "query_tokens": n_tok,
+                   "context": "uniform [98304, 131072]", "topk_blocks": topk, "block_tokens": 8,
+                   "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S},
+        "achieved_hbm_gbps": (attn_bytes + idx_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "step_breakdown_ms": {"indexer_topk": idx_ms, "sparse_decode": attn_ms},
+        "algorithmic_bytes": {"indexer_topk": idx_bytes, "sparse_decode": attn_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "kernel": "attention_kernel<false> (sa_sparse_decode)"},
+    }
+    if cold_ms is not None:
+        result["cold_cache"] = {"ms_per_step": cold_ms, "sparse_decode_ms": cold_attn_ms,
+                                "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, sel_host)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

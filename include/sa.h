@@ -1,0 +1,176 @@
+/*
+ * sa.h -- C ABI of libsa.so: block-indexed sparse GQA decode for MI355X (gfx950).
+ *
+ * The operation is the sparse layer and the sliding-window layer of the hybrid
+ * attention described in "Step 5 Preview: Day-0 Inference and RL Support with
+ * SGLang and Miles" (SGLang blog), sections "Hybrid Attention" and "Kernels from
+ * StepFun", with the shapes of the config table in the Step 5 Preview
+ * open-weights blog (section "What the config says"):
+ *   64 query heads, 4 KV groups (head h reads group h / 16), head dim 192 for K
+ *   and V, one 256-dim index key per 8-token block, top 512 blocks, a 512-token
+ *   window, and a bf16 cache paged in 64-token pages.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked "device" are HIP device pointers owned by the caller. The
+ *   library never allocates, frees or synchronises; all work is enqueued on
+ *   `stream` and the call returns before it runs.
+ * - The return value reports host-side validation (null pointers, sizes,
+ *   alignment, supported shapes, workspace size) and launch errors
+ *   (SA_ERR_HIP). Nothing is enqueued when validation fails.
+ * - Device-side data (page-table entries, positions, sequence ids, selected
+ *   block ids) are not read by the host. A token whose sequence id is outside
+ *   [0, batch) or whose position is outside [0, seq_len) gets no attended tokens:
+ *   its selection row is all -1 and its output row is zero with lse = -inf. A
+ *   page id outside [0, num_pages) or a selected block id outside
+ *   [0, floor(p/8)) is skipped. No such value causes an out-of-bounds access.
+ * - n_tok == 0 is a valid no-op. A token with no earlier complete block
+ *   (p < 8) selects nothing and attends its own block only.
+ * - Results are deterministic: the same inputs and arguments give bitwise
+ *   identical outputs, and a token's outputs do not depend on the other tokens
+ *   of the call when num_splits is given explicitly.
+ * - All arrays are dense and row-major; device pointers must be 16-byte aligned.
+ *
+ * Cache layouts (this library's storage format; the pages fix none):
+ * - K cache  bf16 [num_pages][4 groups][8 blocks][24 dim-chunks][8 tokens][8 dims]
+ * - V cache  bf16 [num_pages][4 groups][8 blocks][192 dims][8 tokens]
+ * - index-key cache bf16 [num_pages][8 blocks][256]
+ *   Token position p of sequence b lives in physical page page_table[b][p / 64],
+ *   block (p % 64) / 8 of that page, token p % 8 of that block.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_NUM_HEADS 64
+#define SA_NUM_GROUPS 4
+#define SA_HEAD_DIM 192
+#define SA_INDEX_DIM 256
+#define SA_BLOCK_TOKENS 8
+#define SA_PAGE_TOKENS 64
+#define SA_MAX_TOPK 512
+#define SA_MAX_WINDOW 4096
+#define SA_MAX_SPLITS 64
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment */
+  SA_ERR_UNSUPPORTED = 2,   /* a shape or constant outside what the kernels support */
+  SA_ERR_WORKSPACE = 3,     /* workspace smaller than the *_workspace_size() answer */
+  SA_ERR_HIP = 4            /* a HIP launch error */
+} sa_status;
+
+/* One paged cache, shared by all calls of a layer.
+ * page_table: device int32 [batch][max_pages_per_seq], physical page ids.
+ * seq_lens:   device int32 [batch], tokens in the cache including the query tokens.
+ * A sequence's query tokens are its last positions (an MTP verify token at
+ * p + j sees the draft tokens p .. p + j - 1). */
+typedef struct {
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int batch;
+  int max_pages_per_seq;
+  int num_pages;
+} sa_paged_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* sa_status_string(sa_status s);
+
+/* Bytes of device workspace sa_indexer_topk needs for these sizes. */
+size_t sa_indexer_topk_workspace_size(int n_tok, int max_pages_per_seq, int topk);
+
+/*
+ * Indexer score + top-k block select.
+ * (SGLang blog, "Hybrid Attention": score 8-token block summaries and keep up to
+ *  512 historical blocks; "Kernels from StepFun": the indexer scores each query
+ *  against compressed history in the paged cache.)
+ *
+ * For query token t at position p = q_pos[t] of sequence b = q_seq[t], with
+ * cb = p / 8, every historical block beta < cb is scored as the fp32 dot product
+ * s = sum_d q_idx[t][d] * k_idx_cache[page_table[b][beta / 8]][beta % 8][d]. The
+ * min(topk, cb) blocks with the largest s are kept; ties go to the lower block
+ * id. The current block is not a candidate (the attention adds it).
+ *
+ * q_idx        device bf16 [n_tok][256]
+ * k_idx_cache  device bf16 [num_pages][8][256]
+ * q_seq, q_pos device int32 [n_tok]
+ * topk         1 .. 512
+ * sel_idx      device int32 [n_tok][topk], out: ascending block ids, -1 padded
+ * workspace    device scratch of at least sa_indexer_topk_workspace_size() bytes,
+ *              256-byte aligned; its contents on entry do not matter.
+ * Exact for index inputs whose partial sums are exact in fp32 (for example
+ * small integers); otherwise scores carry fp32 rounding.
+ */
+sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_desc pd,
+                          const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
+                          int32_t* sel_idx, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Number of partitions a decode call uses for a given request
+ * (num_splits > 0 is returned clamped to SA_MAX_SPLITS; 0 picks from n_tok and
+ * max_blocks_per_token so that the grid fills the GPU). */
+int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits);
+
+/*
+ * Block-sparse GQA attention over the selected blocks and the current block.
+ * (SGLang blog, "Hybrid Attention"; "Kernels from StepFun": decode attention
+ *  over only the selected blocks, partitions merged afterwards.)
+ *
+ * Token t attends the tokens of its selected blocks (sel_idx[t][i] in
+ * [0, p / 8)) and of its current block up to p. Head h uses KV group h / 16:
+ * logit = softmax_scale * <q[t][h], K[j]>, exact softmax, O = sum w_j V[j].
+ *
+ * q            device bf16 [n_tok][64][192]
+ * k_cache, v_cache  device bf16, layouts above
+ * sel_idx      device int32 [n_tok][topk] (as written by sa_indexer_topk)
+ * num_splits   partitions per (token, group); 0 = sa_resolve_num_splits(n_tok, topk + 1, 0)
+ * part_o, part_lse  device fp32 [n_tok][S][64][192], [n_tok][S][64]; needed when
+ *              the resolved S > 1, ignored (may be NULL) when S == 1
+ * out          device bf16 [n_tok][64][192] (round to nearest even) or NULL;
+ *              when S > 1 and out is non-NULL the merge is enqueued too, when
+ *              out is NULL only the partitions are written
+ * out_lse      device fp32 [n_tok][64] natural-log lse, or NULL
+ */
+sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                           sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
+                           const int32_t* sel_idx, int n_tok, int topk, float softmax_scale,
+                           int num_splits, float* part_o, float* part_lse, void* out,
+                           float* out_lse, hipStream_t stream);
+
+/*
+ * Sliding-window GQA attention: token t at position p attends positions
+ * max(0, p - window + 1) .. p. (SGLang blog, "Hybrid Attention": three of
+ * every four layers read the latest 512 tokens.) Arguments as sa_sparse_decode;
+ * window 1 .. SA_MAX_WINDOW; num_splits 0 = sa_resolve_num_splits(n_tok,
+ * window / 8 + 2, 0).
+ */
+sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
+                        sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
+                        int n_tok, int window, float softmax_scale, int num_splits,
+                        float* part_o, float* part_lse, void* out, float* out_lse,
+                        hipStream_t stream);
+
+/*
+ * Merge of per-partition results (SGLang blog, "Kernels from StepFun").
+ * With M = max_s lse_s: O = sum_s e^(lse_s - M) O_s / sum_s e^(lse_s - M),
+ * lse = M + ln sum_s e^(lse_s - M). Partitions with lse = -inf carry no weight;
+ * if all are empty the output is 0 and lse = -inf.
+ * part_o device fp32 [n_tok][num_splits][num_heads][head_dim]; part_lse
+ * [n_tok][num_splits][num_heads]; out device bf16 [n_tok][num_heads][head_dim];
+ * out_lse fp32 [n_tok][num_heads] or NULL. head_dim must be a multiple of 4
+ * and at most 1024; num_heads at most 1024; num_splits 1 .. SA_MAX_SPLITS.
+ */
+sa_status sa_merge(const float* part_o, const float* part_lse, int n_tok, int num_splits,
+                   int num_heads, int head_dim, void* out, float* out_lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

@@ -1,0 +1,200 @@
+// C ABI of libsa.so: host-side validation and launch policy. Every entry point
+// only checks its arguments and enqueues kernels on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "sa_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kMaxPagesPerSeq = 1 << 20;   // positions stay below 2^26
+constexpr int kMaxPoolPages = 1 << 25;     // (page * 4 + group) * 8 + block fits in int32
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+sa_status check_desc(const sa_paged_desc& pd) {
+  if (pd.page_table == nullptr || pd.seq_lens == nullptr) return SA_ERR_INVALID_ARG;
+  if (!aligned(pd.page_table, 4) || !aligned(pd.seq_lens, 4)) return SA_ERR_INVALID_ARG;
+  if (pd.batch < 1 || pd.max_pages_per_seq < 1 || pd.num_pages < 1) return SA_ERR_INVALID_ARG;
+  if (pd.max_pages_per_seq > kMaxPagesPerSeq || pd.num_pages > kMaxPoolPages) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+sa_status check_tokens(const int32_t* q_seq, const int32_t* q_pos) {
+  if (q_seq == nullptr || q_pos == nullptr) return SA_ERR_INVALID_ARG;
+  if (!aligned(q_seq, 4) || !aligned(q_pos, 4)) return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
+sa_status decode_common(const void* q, const void* k_cache, const void* v_cache, const sa_paged_desc& pd,
+                        const int32_t* q_seq, const int32_t* q_pos, int n_tok, float softmax_scale,
+                        int max_blocks, int num_splits, float* part_o, float* part_lse, void* out,
+                        float* out_lse, bool window_mode, const int32_t* sel_idx, int topk, int window,
+                        hipStream_t stream) {
+  if (n_tok < 0 || num_splits < 0) return SA_ERR_INVALID_ARG;
+  if (n_tok == 0) return SA_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr) return SA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return SA_ERR_INVALID_ARG;
+  sa_status st = check_desc(pd);
+  if (st != SA_OK) return st;
+  if ((st = check_tokens(q_seq, q_pos)) != SA_OK) return st;
+  if (!isfinite(softmax_scale)) return SA_ERR_INVALID_ARG;
+  if (num_splits > SA_MAX_SPLITS) return SA_ERR_UNSUPPORTED;
+  const int S = sa_resolve_num_splits(n_tok, max_blocks, num_splits);
+  if (S == 1 && out == nullptr) return SA_ERR_INVALID_ARG;
+  if (S > 1 && (part_o == nullptr || part_lse == nullptr)) return SA_ERR_INVALID_ARG;
+  if (out != nullptr && !aligned(out, 16)) return SA_ERR_INVALID_ARG;
+  if (part_o != nullptr && !aligned(part_o, 16)) return SA_ERR_INVALID_ARG;
+  if (part_lse != nullptr && !aligned(part_lse, 4)) return SA_ERR_INVALID_ARG;
+  if (out_lse != nullptr && !aligned(out_lse, 4)) return SA_ERR_INVALID_ARG;
+
+  sa::AttnArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.page_table = pd.page_table;
+  a.seq_lens = pd.seq_lens;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.sel_idx = sel_idx;
+  a.n_tok = n_tok;
+  a.topk = topk;
+  a.window = window;
+  a.num_splits = S;
+  a.batch = pd.batch;
+  a.max_pages = pd.max_pages_per_seq;
+  a.num_pages = pd.num_pages;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.part_o = S > 1 ? part_o : nullptr;
+  a.part_lse = S > 1 ? part_lse : nullptr;
+  a.out = S == 1 ? static_cast<uint16_t*>(out) : nullptr;
+  a.out_lse = S == 1 ? out_lse : nullptr;
+  if (sa::launch_attention(a, window_mode, stream) != hipSuccess) return SA_ERR_HIP;
+  if (S > 1 && out != nullptr) {
+    if (sa::launch_merge(part_o, part_lse, n_tok, S, sa::kHeads, sa::kHeadDim, static_cast<uint16_t*>(out),
+                         out_lse, stream) != hipSuccess)
+      return SA_ERR_HIP;
+  }
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARG: return "SA_ERR_INVALID_ARG";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+  }
+  return "SA_ERR_UNKNOWN";
+}
+
+size_t sa_indexer_topk_workspace_size(int n_tok, int max_pages_per_seq, int topk) {
+  (void)topk;
+  if (n_tok <= 0 || max_pages_per_seq <= 0) return 0;
+  return sa::indexer_workspace_layout(n_tok, max_pages_per_seq).total;
+}
+
+int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits) {
+  if (num_splits > 0) return std::min(num_splits, SA_MAX_SPLITS);
+  // Fill the GPU: aim for about 1024 workgroups (4 per CU) while giving every
+  // wave of a workgroup at least one 4-block chunk.
+  const int work = std::max(1, n_tok) * sa::kGroups;
+  const int want = (1024 + work - 1) / work;
+  const int chunks = (std::max(1, max_blocks_per_token) + 3) / 4;
+  const int cap = std::max(1, chunks / 4);
+  return std::max(1, std::min(std::min(want, cap), SA_MAX_SPLITS));
+}
+
+sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_desc pd, const int32_t* q_seq,
+                          const int32_t* q_pos, int n_tok, int topk, int32_t* sel_idx, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (n_tok < 0) return SA_ERR_INVALID_ARG;
+  if (n_tok == 0) return SA_OK;
+  if (q_idx == nullptr || k_idx_cache == nullptr || sel_idx == nullptr || workspace == nullptr)
+    return SA_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(k_idx_cache, 16) || !aligned(sel_idx, 4) || !aligned(workspace, 256))
+    return SA_ERR_INVALID_ARG;
+  sa_status st = check_desc(pd);
+  if (st != SA_OK) return st;
+  if ((st = check_tokens(q_seq, q_pos)) != SA_OK) return st;
+  if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
+  const sa::IndexerWorkspace w = sa::indexer_workspace_layout(n_tok, pd.max_pages_per_seq);
+  if (ws_bytes < w.total) return SA_ERR_WORKSPACE;
+
+  sa::IndexerArgs a;
+  a.q_idx = static_cast<const uint8_t*>(q_idx);
+  a.k_idx_cache = static_cast<const uint8_t*>(k_idx_cache);
+  a.page_table = pd.page_table;
+  a.seq_lens = pd.seq_lens;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.n_tok = n_tok;
+  a.topk = topk;
+  a.batch = pd.batch;
+  a.max_pages = pd.max_pages_per_seq;
+  a.num_pages = pd.num_pages;
+  a.max_hist_blocks = pd.max_pages_per_seq * sa::kBlocksPerPage;
+  // Query tokens of one sequence are scored in one pass over its keys; the
+  // group size guesses how many consecutive tokens share a sequence (any guess
+  // is correct, a good one reads each key once).
+  a.group_size = std::max(1, std::min(4, n_tok / pd.batch));
+  const int ngroups = (n_tok + a.group_size - 1) / a.group_size;
+  int chunk = 4096;
+  while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  a.chunk_blocks = chunk;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
+  a.cand_count = reinterpret_cast<uint32_t*>(ws + w.count_off);
+  a.scores = reinterpret_cast<float*>(ws + w.scores_off);
+  a.cand = reinterpret_cast<uint2*>(ws + w.cand_off);
+  a.sel_idx = sel_idx;
+  if (sa::launch_indexer_topk(a, stream) != hipSuccess) return SA_ERR_HIP;
+  return SA_OK;
+}
+
+sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,
+                           const int32_t* q_seq, const int32_t* q_pos, const int32_t* sel_idx, int n_tok,
+                           int topk, float softmax_scale, int num_splits, float* part_o, float* part_lse,
+                           void* out, float* out_lse, hipStream_t stream) {
+  if (n_tok > 0) {
+    if (sel_idx == nullptr || !aligned(sel_idx, 4)) return SA_ERR_INVALID_ARG;
+    if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
+  }
+  return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
+                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, stream);
+}
+
+sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,
+                        const int32_t* q_seq, const int32_t* q_pos, int n_tok, int window, float softmax_scale,
+                        int num_splits, float* part_o, float* part_lse, void* out, float* out_lse,
+                        hipStream_t stream) {
+  if (n_tok > 0 && (window < 1 || window > SA_MAX_WINDOW)) return SA_ERR_UNSUPPORTED;
+  return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, window / 8 + 2, num_splits,
+                       part_o, part_lse, out, out_lse, true, nullptr, 0, window, stream);
+}
+
+sa_status sa_merge(const float* part_o, const float* part_lse, int n_tok, int num_splits, int num_heads,
+                   int head_dim, void* out, float* out_lse, hipStream_t stream) {
+  if (n_tok < 0) return SA_ERR_INVALID_ARG;
+  if (n_tok == 0) return SA_OK;
+  if (part_o == nullptr || part_lse == nullptr || out == nullptr) return SA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_heads < 1 || head_dim < 4) return SA_ERR_INVALID_ARG;
+  if (num_splits > SA_MAX_SPLITS || num_heads > 1024 || head_dim > 1024 || head_dim % 4 != 0)
+    return SA_ERR_UNSUPPORTED;
+  if (!aligned(part_o, 16) || !aligned(part_lse, 4) || !aligned(out, 8)) return SA_ERR_INVALID_ARG;
+  if (out_lse != nullptr && !aligned(out_lse, 4)) return SA_ERR_INVALID_ARG;
+  if (sa::launch_merge(part_o, part_lse, n_tok, num_splits, num_heads, head_dim, static_cast<uint16_t*>(out),
+                       out_lse, stream) != hipSuccess)
+    return SA_ERR_HIP;
+  return SA_OK;
+}
+
+}  // extern "C"

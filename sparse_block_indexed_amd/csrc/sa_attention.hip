@@ -1,0 +1,327 @@
+// Block-gather GQA decode attention for gfx950: the sparse layer (selected
+// blocks + current block) and the sliding-window layer share one kernel.
+//
+// What is computed: SGLang blog "Step 5 Preview: Day-0 Inference and RL Support
+// with SGLang and Miles", section "Hybrid Attention" (exact attention over the
+// tokens of up to 512 chosen earlier blocks plus the current block; three of
+// four layers read the latest 512 tokens) and section "Kernels from StepFun"
+// (decode attention over the selected blocks only, cut into partitions whose
+// partial results are merged).  Shapes: open-weights blog config table (64 query
+// heads, 4 KV groups, head dim 192).
+//
+// Work decomposition.  One workgroup of 4 waves owns one (query token, KV
+// group, partition).  The partition's block list (logical block id and
+// physical cache unit per slot) is resolved once into LDS.  The waves take
+// 32-token chunks (4 blocks) round-robin; each wave keeps its own online-softmax
+// state for the 16 heads of the group, and the 4 wave states are merged in LDS
+// in a fixed order at the end (deterministic).
+//
+// MFMA mapping (v_mfma_f32_16x16x32_bf16, A: lane l holds row l%16, k-slice
+// l/16; B: lane l holds column l%16, same k-slice; D: lane l holds rows
+// 4*(l/16)+r, column l%16):
+//   scores  S^T[token][head] = K[token][:] . Q[head][:]   (two 16-token halves)
+//           A = K rows straight from the cache (16 B per lane per k-step),
+//           B = Q of the 16 heads, loaded once.
+//   output  O^T[dim][head] += V^T[dim][token] . P^T[token][head]
+//           A = V from the cache (the V layout keeps 8 tokens of one dim in 16 B),
+//           B = P: each lane already holds the 8 probabilities of "its" block for
+//           "its" head, so no data moves between lanes.
+// Token order inside a chunk is chosen so that the rows of the score half-tiles
+// land in exactly the lanes the PV step needs them in (half s, row 4*j + r <->
+// block j, token 4*s + r).
+
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxSlots = SA_MAX_TOPK + 1 > SA_MAX_WINDOW / 8 + 2 ? SA_MAX_TOPK + 1 : SA_MAX_WINDOW / 8 + 2;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 of differences never sees inf-inf
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool kWindow>
+__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
+  __shared__ int32_t s_unit[kMaxSlots];
+  __shared__ int32_t s_beta[kMaxSlots];
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ float s_e[kWaves][16];
+  __shared__ f32x4 s_o[kWaves - 1][12][64];
+
+  const int S = a.num_splits;
+  const int wg = blockIdx.x;
+  const int sp = wg % S;
+  const int g = (wg / S) % kGroups;
+  const int t = wg / (S * kGroups);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lq = lane & 15;
+  const int lg = lane >> 4;
+
+  // ---- token and its attended block list --------------------------------
+  const int b = a.q_seq[t];
+  const int p = a.q_pos[t];
+  bool valid = b >= 0 && b < a.batch && p >= 0;
+  if (valid) valid = p < a.seq_lens[b] && p < a.max_pages * kPageTokens;
+  const int cb = valid ? (p >> 3) : 0;
+  int nslots = 0, lo = 0, b_lo = 0, nsel = 0;
+  if (valid) {
+    if (kWindow) {
+      lo = max(0, p - a.window + 1);
+      b_lo = lo >> 3;
+      nslots = cb - b_lo + 1;
+    } else {
+      nsel = min(a.topk, cb);
+      nslots = nsel + 1;
+    }
+  }
+  const int s0 = (int)(((long long)sp * nslots) / S);
+  const int s1 = (int)(((long long)(sp + 1) * nslots) / S);
+  const int n = s1 - s0;
+
+  for (int i = tid; i < n; i += kThreads) {
+    const int slot = s0 + i;
+    int beta;
+    bool ok = true;
+    if (kWindow) {
+      beta = b_lo + slot;
+    } else if (slot < nsel) {
+      beta = a.sel_idx[(size_t)t * a.topk + slot];
+      ok = beta >= 0 && beta < cb;
+    } else {
+      beta = cb;
+    }
+    int unit = -1;
+    if (ok) {
+      const int page = a.page_table[(size_t)b * a.max_pages + (beta >> 3)];
+      if (page >= 0 && page < a.num_pages)
+        unit = (page * kGroups + g) * kBlocksPerPage + (beta & 7);
+    }
+    s_unit[i] = unit;
+    s_beta[i] = ok ? beta : 0;
+  }
+  __syncthreads();
+
+  // ---- per-wave streaming loop -------------------------------------------
+  // Q of head 16g + lq, dim chunks 6*lg .. 6*lg+5 (B operand of the score MFMA)
+  u32x4 qv[6];
+  {
+    const uint8_t* qrow = a.q + ((size_t)t * kHeads + g * kHeadsPerGroup + lq) * (kHeadDim * 2) + lg * 6 * 16;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) qv[i] = valid ? load16(qrow + i * 16) : u32x4{0, 0, 0, 0};
+  }
+  const float sc = a.scale_log2;
+  const int nchunks = (n + 3) >> 2;
+  float m_run = kNegBig;
+  float l_run = 0.f;   // sum of the bf16-rounded probabilities (normalises O)
+  float e_run = 0.f;   // sum of the unrounded probabilities (gives lse)
+  f32x4 acc[12];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // K lane offset inside a unit: dim chunk 6*lg (+i), token (lq & 3) (+4 for half 1)
+  const uint8_t* kbase = a.k_cache + lg * 6 * 128 + (lq & 3) * 16;
+  // V lane offset inside a unit: dim lq (+16 per output tile), all 8 tokens
+  const uint8_t* vbase = a.v_cache + lq * 16;
+
+  u32x4 kr[2][6];
+  u32x4 vr[12];
+
+  auto load_k = [&](int c) {
+    const int slot = 4 * c + (lq >> 2);
+    const int unit = slot < n ? s_unit[slot] : -1;
+    if (unit >= 0) {
+      const uint8_t* pk = kbase + (size_t)unit * kUnitBytes;
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        kr[0][i] = load16(pk + i * 128);
+        kr[1][i] = load16(pk + i * 128 + 64);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) kr[0][i] = kr[1][i] = u32x4{0, 0, 0, 0};
+    }
+  };
+  auto load_v = [&](int c) {
+    const int slot = 4 * c + lg;
+    const int unit = slot < n ? s_unit[slot] : -1;
+    if (unit >= 0) {
+      const uint8_t* pv = vbase + (size_t)unit * kUnitBytes;
+#pragma unroll
+      for (int i = 0; i < 12; ++i) vr[i] = load16(pv + i * 256);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 12; ++i) vr[i] = u32x4{0, 0, 0, 0};
+    }
+  };
+
+  int c = wave;
+  if (c < nchunks) {
+    load_k(c);
+    load_v(c);
+  }
+  for (; c < nchunks; c += kWaves) {
+    f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      st0 = mfma_bf16(kr[0][i], qv[i], st0);
+      st1 = mfma_bf16(kr[1][i], qv[i], st1);
+    }
+    const int cn = c + kWaves;
+    if (cn < nchunks) load_k(cn);
+
+    // this lane's block (lg) of the chunk and its valid positions
+    const int slot = 4 * c + lg;
+    const bool blk_ok = slot < n && s_unit[slot] >= 0;
+    const int pos0 = (slot < n ? s_beta[slot] : 0) * kBlockTokens;
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = st0[r] * sc;
+      x[4 + r] = st1[r] * sc;
+    }
+    uint32_t okmask = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok = blk_ok && (pos0 + k <= p) && (pos0 + k >= lo);
+      okmask |= ok ? (1u << k) : 0u;
+      x[k] = ok ? x[k] : -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float pr[8];
+    float esum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pr[k] = __builtin_amdgcn_exp2f(x[k] - m_new);
+      esum += pr[k];
+    }
+    const u32x4 pb = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+    // the row sum uses the same rounded probabilities the PV product sees, so
+    // the weights are normalised consistently
+    float psum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      psum += __uint_as_float(pb[w] << 16) + __uint_as_float(pb[w] & 0xffff0000u);
+    l_run = l_run * alpha + psum;
+    e_run = e_run * alpha + esum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc[i] *= alpha;
+
+    // Positions outside the attended range inside a loaded block (the current
+    // block past p, the window's first block before lo) may hold anything;
+    // zero their V so that 0-probability never meets a non-finite value.
+    if (__any(blk_ok && okmask != 0xffu)) {
+      u32x4 vm;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo16 = (okmask >> (2 * w)) & 1u ? 0x0000ffffu : 0u;
+        const uint32_t hi16 = (okmask >> (2 * w + 1)) & 1u ? 0xffff0000u : 0u;
+        vm[w] = lo16 | hi16;
+      }
+#pragma unroll
+      for (int i = 0; i < 12; ++i) vr[i] &= vm;
+    }
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc[i] = mfma_bf16(vr[i], pb, acc[i]);
+    if (cn < nchunks) load_v(cn);
+  }
+
+  // ---- merge the 4 wave states (fixed order) and write -------------------
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  float e_tot = e_run + __shfl_xor(e_run, 16);
+  e_tot += __shfl_xor(e_tot, 32);
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 12; ++i) s_o[wave - 1][i][lane] = acc[i];
+  }
+  if (lg == 0) {
+    s_m[wave][lq] = m_run;
+    s_l[wave][lq] = l_tot;
+    s_e[wave][lq] = e_tot;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  float M = m_run;
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][lq]);
+  const float a0 = __builtin_amdgcn_exp2f(m_run - M);
+  float L = l_tot * a0;
+  float E = e_tot * a0;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) acc[i] *= a0;
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    const float aw = __builtin_amdgcn_exp2f(s_m[w][lq] - M);
+    L += s_l[w][lq] * aw;
+    E += s_e[w][lq] * aw;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc[i] += s_o[w - 1][i][lane] * aw;
+  }
+  const bool any = L > 0.f;
+  const float inv = any ? 1.0f / L : 0.f;
+  const float lse = any ? (M + __builtin_amdgcn_logf(E)) * kLn2 : -INFINITY;
+  const int head = g * kHeadsPerGroup + lq;
+
+  if (S == 1) {
+    uint16_t* orow = a.out + ((size_t)t * kHeads + head) * kHeadDim + 4 * lg;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      uint2 v;
+      v.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+      v.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * i) = v;
+    }
+    if (a.out_lse != nullptr && lg == 0) a.out_lse[(size_t)t * kHeads + head] = lse;
+  } else {
+    float* orow = a.part_o + (((size_t)t * S + sp) * kHeads + head) * kHeadDim + 4 * lg;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = acc[i] * inv;
+    if (lg == 0) a.part_lse[((size_t)t * S + sp) * kHeads + head] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, bool window_mode, hipStream_t stream) {
+  if (a.n_tok == 0) return hipSuccess;
+  const long long grid = (long long)a.n_tok * kGroups * a.num_splits;
+  if (window_mode)
+    attention_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
+  else
+    attention_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,85 @@
+// Internal declarations shared by the HIP translation units of libsa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sa.h"
+
+namespace sa {
+
+constexpr int kHeads = SA_NUM_HEADS;
+constexpr int kGroups = SA_NUM_GROUPS;
+constexpr int kHeadsPerGroup = kHeads / kGroups;
+constexpr int kHeadDim = SA_HEAD_DIM;
+constexpr int kIdxDim = SA_INDEX_DIM;
+constexpr int kBlockTokens = SA_BLOCK_TOKENS;
+constexpr int kPageTokens = SA_PAGE_TOKENS;
+constexpr int kBlocksPerPage = kPageTokens / kBlockTokens;
+constexpr int kUnitBytes = kBlockTokens * kHeadDim * 2;   // one (page, group, block) of K or V
+constexpr int kKeyBytes = kIdxDim * 2;                     // one index key
+
+// indexer workspace
+constexpr int kHistBins = 2048;       // first radix digit: key bits 31..21
+constexpr int kCandCap = 4096;        // candidates kept per token for the in-LDS finish
+constexpr int kCollectChunk = 4096;   // scores per collect workgroup
+
+struct AttnArgs {
+  const uint8_t* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* sel_idx;   // sparse mode only
+  int n_tok;
+  int topk;                 // sparse mode
+  int window;               // window mode
+  int num_splits;
+  int batch;
+  int max_pages;
+  int num_pages;
+  float scale_log2;         // softmax_scale * log2(e)
+  float* part_o;            // used when num_splits > 1
+  float* part_lse;
+  uint16_t* out;            // used when num_splits == 1
+  float* out_lse;
+};
+
+struct IndexerArgs {
+  const uint8_t* q_idx;
+  const uint8_t* k_idx_cache;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int n_tok;
+  int topk;
+  int batch;
+  int max_pages;
+  int num_pages;
+  int max_hist_blocks;      // max_pages * 8: stride of the score rows
+  int group_size;           // query tokens scored per pass over a sequence's keys
+  int chunk_blocks;         // blocks per score workgroup
+  int32_t* sel_idx;
+  uint32_t* hist;           // [n_tok][kHistBins]
+  uint32_t* cand_count;     // [n_tok]
+  float* scores;            // [n_tok][max_hist_blocks]
+  uint2* cand;              // [n_tok][kCandCap] (key, block)
+};
+
+struct IndexerWorkspace {
+  size_t hist_off, count_off, scores_off, cand_off, total;
+};
+
+IndexerWorkspace indexer_workspace_layout(int n_tok, int max_pages_per_seq);
+
+hipError_t launch_attention(const AttnArgs& a, bool window_mode, hipStream_t stream);
+hipError_t launch_merge(const float* part_o, const float* part_lse, int n_tok, int num_splits,
+                        int num_heads, int head_dim, uint16_t* out, float* out_lse,
+                        hipStream_t stream);
+hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream);
+
+}  // namespace sa

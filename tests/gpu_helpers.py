@@ -1,0 +1,102 @@
+"""Helpers for the GPU parity tests: run the library through its binding and
+compute the oracle's answer for the same device-resident inputs, reading back
+only the pages each token needs."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import sa_oracle as O
+from sparse_block_indexed_amd import inputs as I
+
+SCALE = 1.0 / math.sqrt(192.0)
+MAX_ABS = 2e-2
+REL_RMS = 5e-3
+LSE_ABS = 1e-3
+
+
+def device_tables(wl, device="cuda"):
+    return wl.device_ints(device)
+
+
+def run_sparse_layer(wl, topk=512, num_splits=0, scale=SCALE, tabs=None):
+    from sparse_block_indexed_amd import ops
+    pt, sl, qs, qp = tabs if tabs is not None else device_tables(wl)
+    sel = ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk)
+    out, lse = ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return sel, out, lse
+
+
+def run_swa(wl, window=512, num_splits=0, scale=SCALE, tabs=None):
+    from sparse_block_indexed_amd import ops
+    pt, sl, qs, qp = tabs if tabs is not None else device_tables(wl)
+    out, lse = ops.swa_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, window, scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+class OracleView:
+    """Host-side oracle over a device workload; caches each sequence's index keys."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        self._keys = {}
+
+    def keys(self, b, cb):
+        have = self._keys.get(b)
+        if have is None or have.shape[0] < cb:
+            npg = (cb + 7) // 8
+            pages = torch.as_tensor(self.wl.page_table[b, :npg].astype(np.int64), device=self.wl.k_idx_cache.device)
+            kidx = I.bf16_bits(self.wl.k_idx_cache.index_select(0, pages))
+            have = O.index_keys(kidx, np.arange(npg), npg * 8)
+            self._keys[b] = have
+        return have[:cb]
+
+    def selection(self, t, topk=512):
+        b, p = int(self.wl.q_seq[t]), int(self.wl.q_pos[t])
+        cb = p // 8
+        q = O.bf16_to_f64(I.bf16_bits(self.wl.q_idx[t]))
+        return O.indexer_topk_token(q, self.keys(b, cb), topk)
+
+    def attention(self, t, positions, scale=SCALE):
+        wl = self.wl
+        b = int(wl.q_seq[t])
+        row = wl.page_table[b]
+        logical = np.unique(np.asarray(positions) // 64)
+        phys = row[logical].astype(np.int64)
+        dev = wl.k_cache.device
+        idx = torch.as_tensor(phys, device=dev)
+        kc = I.bf16_bits(wl.k_cache.index_select(0, idx))
+        vc = I.bf16_bits(wl.v_cache.index_select(0, idx))
+        compact = np.full(row.shape[0], -1, dtype=np.int64)
+        compact[logical] = np.arange(len(logical))
+        return O.attend_positions(O.bf16_to_f64(I.bf16_bits(wl.q[t])), kc, vc, compact, positions, scale)
+
+    def sparse(self, t, sel, scale=SCALE):
+        return self.attention(t, O.sparse_token_positions(np.asarray(sel), int(self.wl.q_pos[t])), scale)
+
+    def swa(self, t, window=512, scale=SCALE):
+        return self.attention(t, O.window_positions(int(self.wl.q_pos[t]), window), scale)
+
+
+def bf16_to_np(t: torch.Tensor) -> np.ndarray:
+    return O.bf16_to_f64(I.bf16_bits(t))
+
+
+def assert_close_outputs(got_out, got_lse, ref_out, ref_lse, what=""):
+    """Spec tolerance: max-abs 2e-2 and relative RMS 5e-3 over the compared set;
+    lse within 1e-3."""
+    got_out = np.asarray(got_out, dtype=np.float64)
+    ref_out = np.asarray(ref_out, dtype=np.float64)
+    assert np.isfinite(got_out).all(), f"{what}: non-finite output"
+    err = np.abs(got_out - ref_out)
+    rel = np.sqrt((err ** 2).sum()) / max(np.sqrt((ref_out ** 2).sum()), 1e-300)
+    assert err.max() <= MAX_ABS, f"{what}: max abs {err.max():.3e}"
+    assert rel <= REL_RMS, f"{what}: rel rms {rel:.3e}"
+    if got_lse is not None:
+        dl = np.abs(np.asarray(got_lse, dtype=np.float64) - np.asarray(ref_lse, dtype=np.float64))
+        assert dl.max() <= LSE_ABS, f"{what}: lse max abs {dl.max():.3e}"
+    return err.max(), rel

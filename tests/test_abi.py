@@ -1,0 +1,154 @@
+"""The C ABI on the host: the library loads, exports every function the header
+declares, and rejects bad arguments with the documented status before touching
+the device (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_block_indexed_amd import ops
+    if not os.path.exists(ops.LIB_PATH):
+        from sparse_block_indexed_amd import build
+        build.build()
+    return ops.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["sa_indexer_topk", "sa_sparse_decode", "sa_swa_decode", "sa_merge",
+              "sa_indexer_topk_workspace_size", "sa_status_string", "sa_resolve_num_splits"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    from sparse_block_indexed_amd import ops
+    assert lib.sa_status_string(ops.SA_OK) == b"SA_OK"
+    assert lib.sa_status_string(ops.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
+    assert lib.sa_status_string(99) == b"SA_ERR_UNKNOWN"
+
+
+def test_workspace_size(lib):
+    assert lib.sa_indexer_topk_workspace_size(0, 16, 512) == 0
+    a = lib.sa_indexer_topk_workspace_size(1, 128, 512)
+    b = lib.sa_indexer_topk_workspace_size(2, 128, 512)
+    c = lib.sa_indexer_topk_workspace_size(2, 256, 512)
+    assert 0 < a < b < c
+    assert a % 256 == 0
+    # scores (4 B per historical block) + 2048-bin histogram + candidates per token
+    assert a >= 128 * 8 * 4 + 2048 * 4 + 4096 * 8
+
+
+def test_resolve_num_splits(lib):
+    r = lib.sa_resolve_num_splits
+    assert r(256, 513, 0) == 1          # 128K verify batch: the grid already fills the GPU
+    assert r(1, 513, 0) == 32           # one token: spread its 129 chunks over 32 partitions
+    assert r(64, 66, 0) == 4            # sliding window, batch 64
+    assert r(4, 513, 0) == 32
+    assert r(1, 1, 0) == 1              # nothing to split
+    assert r(3, 513, 7) == 7            # explicit value kept
+    assert r(3, 513, 1000) == 64        # clamped
+
+
+def _desc(ops, batch=1, max_pages=16, num_pages=16, pt=0x1000, sl=0x2000):
+    return ops.PagedDesc(pt, sl, batch, max_pages, num_pages)
+
+
+P = 0x10000          # an aligned fake device address; never dereferenced by these calls
+
+
+def test_indexer_topk_validation(lib):
+    from sparse_block_indexed_amd import ops
+    d = _desc(ops)
+    ws = lib.sa_indexer_topk_workspace_size(4, 16, 512)
+    f = lib.sa_indexer_topk
+    assert f(None, None, d, None, None, 0, 512, None, None, 0, None) == ops.SA_OK           # n_tok = 0: no-op
+    assert f(P, P, d, P, P, -1, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
+    assert f(None, P, d, P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
+    assert f(P, P, d, P, None, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
+    assert f(P, P, d, P, P, 4, 512, P, None, ws, None) == ops.SA_ERR_INVALID_ARG
+    assert f(P + 8, P, d, P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG         # misaligned
+    assert f(P, P, d, P, P, 4, 512, P, P + 16, ws, None) == ops.SA_ERR_INVALID_ARG        # workspace alignment
+    assert f(P, P, d, P, P, 4, 0, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, d, P, P, 4, 513, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, d, P, P, 4, 512, P, P, ws - 1, None) == ops.SA_ERR_WORKSPACE
+    assert f(P, P, _desc(ops, batch=0), P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
+    assert f(P, P, _desc(ops, pt=0), P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
+    assert f(P, P, _desc(ops, num_pages=1 << 26), P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+
+
+def test_sparse_decode_validation(lib):
+    from sparse_block_indexed_amd import ops
+    d = _desc(ops)
+    f = lib.sa_sparse_decode
+    ok = dict(q=P, k=P, v=P, qs=P, qp=P, sel=P, n=4, topk=512, sc=0.07, S=1, po=None, pl=None, out=P, ol=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], d, a["qs"], a["qp"], a["sel"], a["n"], a["topk"], ctypes.c_float(a["sc"]),
+                 a["S"], a["po"], a["pl"], a["out"], a["ol"], None)
+
+    assert call(n=0, q=None, k=None, v=None, sel=None, out=None) == ops.SA_OK
+    assert call(n=-1) == ops.SA_ERR_INVALID_ARG
+    assert call(q=None) == ops.SA_ERR_INVALID_ARG
+    assert call(sel=None) == ops.SA_ERR_INVALID_ARG
+    assert call(topk=0) == ops.SA_ERR_UNSUPPORTED
+    assert call(topk=600) == ops.SA_ERR_UNSUPPORTED
+    assert call(sc=float("nan")) == ops.SA_ERR_INVALID_ARG
+    assert call(S=-1) == ops.SA_ERR_INVALID_ARG
+    assert call(S=65) == ops.SA_ERR_UNSUPPORTED
+    assert call(out=None) == ops.SA_ERR_INVALID_ARG                    # S == 1 needs out
+    assert call(S=4, po=None, pl=P) == ops.SA_ERR_INVALID_ARG         # S > 1 needs partials
+    assert call(k=P + 4) == ops.SA_ERR_INVALID_ARG                     # misaligned cache
+
+
+def test_swa_and_merge_validation(lib):
+    from sparse_block_indexed_amd import ops
+    d = _desc(ops)
+    f = lib.sa_swa_decode
+    assert f(P, P, P, d, P, P, 0, 512, ctypes.c_float(0.1), 0, None, None, None, None, None) == ops.SA_OK
+    assert f(P, P, P, d, P, P, 2, 0, ctypes.c_float(0.1), 1, None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, P, d, P, P, 2, 5000, ctypes.c_float(0.1), 1, None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
+    m = lib.sa_merge
+    assert m(None, None, 0, 1, 64, 192, None, None, None) == ops.SA_OK
+    assert m(P, P, 2, 0, 64, 192, P, None, None) == ops.SA_ERR_INVALID_ARG
+    assert m(P, P, 2, 65, 64, 192, P, None, None) == ops.SA_ERR_UNSUPPORTED
+    assert m(P, P, 2, 4, 64, 190, P, None, None) == ops.SA_ERR_UNSUPPORTED
+    assert m(None, P, 2, 4, 64, 192, P, None, None) == ops.SA_ERR_INVALID_ARG
+
+
+def test_product_path_refuses_to_run_without_the_library(tmp_path):
+    from sparse_block_indexed_amd import ops
+    saved = ops._lib
+    ops._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            ops.load_library(str(tmp_path / "libsa.so"))
+    finally:
+        ops._lib = saved
+
+
+def test_product_path_does_not_import_the_oracle():
+    import subprocess
+    import sys
+    code = ("import sys; import sparse_block_indexed_amd.ops, sparse_block_indexed_amd.bytes_model, "
+            "sparse_block_indexed_amd.inputs; print(any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "False"

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded, device-resident inputs.
+
+Selections must match bit for bit (index inputs are small integers, so scores
+are exact). Outputs must be within max-abs 2e-2 and relative RMS 5e-3 of the
+oracle, lse within 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sa_oracle as O
+from sparse_block_indexed_amd import inputs as I
+
+from gpu_helpers import (SCALE, OracleView, assert_close_outputs, bf16_to_np, device_tables, run_sparse_layer,
+                         run_swa)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_block_indexed_amd import ops
+    ops.load_library()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_all(wl, sel, out, lse, tokens, topk=512, what=""):
+    ov = OracleView(wl)
+    sel_h = sel.cpu().numpy()
+    outs, refs, lses, rlses = [], [], [], []
+    for t in tokens:
+        ref_sel = ov.selection(t, topk)
+        assert sel_h[t].tolist() == ref_sel.tolist(), f"{what}: token {t} selection differs"
+        ro, rl = ov.sparse(t, ref_sel)
+        outs.append(bf16_to_np(out[t]))
+        lses.append(lse[t].cpu().numpy())
+        refs.append(ro)
+        rlses.append(rl)
+    return assert_close_outputs(np.stack(outs), np.stack(lses), np.stack(refs), np.stack(rlses), what)
+
+
+# a mixed small batch: contexts around every block/page/top-k boundary, 3 verify tokens each
+SMALL = I.WorkloadSpec("small_mixed", batch=12,
+                       seq_lens=[1, 7, 8, 9, 63, 64, 65, 300, 1000, 4103, 4111, 9000],
+                       q_per_seq=3, spare_pages=5)
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_small_mixed_sparse(num_splits):
+    _say(f"small_mixed sparse S={num_splits}")
+    wl = I.make_workload(SMALL, seed=11, device="cuda")
+    sel, out, lse = run_sparse_layer(wl, num_splits=num_splits)
+    _check_all(wl, sel, out, lse, range(wl.n_tok), what=f"small S={num_splits}")
+
+
+@pytest.mark.parametrize("window,num_splits", [(512, 0), (512, 1), (64, 2), (1, 1), (4096, 0)])
+def test_small_mixed_swa(window, num_splits):
+    _say(f"small_mixed swa W={window} S={num_splits}")
+    wl = I.make_workload(SMALL, seed=12, device="cuda")
+    out, lse = run_swa(wl, window=window, num_splits=num_splits)
+    ov = OracleView(wl)
+    refs = [ov.swa(t, window) for t in range(wl.n_tok)]
+    assert_close_outputs(bf16_to_np(out), lse.cpu().numpy(), np.stack([r[0] for r in refs]),
+                         np.stack([r[1] for r in refs]), f"swa W={window}")
+
+
+@pytest.mark.parametrize("topk", [1, 7, 100, 511])
+def test_small_topk_values(topk):
+    _say(f"topk={topk}")
+    wl = I.make_workload(SMALL, seed=13, device="cuda")
+    sel, out, lse = run_sparse_layer(wl, topk=topk)
+    _check_all(wl, sel, out, lse, range(wl.n_tok), topk=topk, what=f"topk={topk}")
+
+
+def test_config0_decode_8k():
+    _say("config 0")
+    wl = I.config_workload(0, device="cuda")
+    sel, out, lse = run_sparse_layer(wl)
+    _check_all(wl, sel, out, lse, range(wl.n_tok), what="decode_8k")
+
+
+def test_config1_mtp_verify_128k():
+    """The headline workload at full size in the bench's launch configuration:
+    every token's selection is checked; attention on a sample of 16 tokens."""
+    _say("config 1")
+    wl = I.config_workload(1, device="cuda")
+    sel, out, lse = run_sparse_layer(wl)
+    ov = OracleView(wl)
+    sel_h = sel.cpu().numpy()
+    for t in range(wl.n_tok):
+        assert sel_h[t].tolist() == ov.selection(t).tolist(), f"token {t}"
+    rng = np.random.default_rng(0)
+    sample = sorted(rng.choice(wl.n_tok, size=16, replace=False).tolist())
+    _check_all(wl, sel, out, lse, sample, what="mtp_verify_128k")
+
+
+def test_config2_swa_32k():
+    _say("config 2")
+    wl = I.config_workload(2, device="cuda")
+    out, lse = run_swa(wl)
+    ov = OracleView(wl)
+    refs = [ov.swa(t) for t in range(wl.n_tok)]
+    assert_close_outputs(bf16_to_np(out), lse.cpu().numpy(), np.stack([r[0] for r in refs]),
+                         np.stack([r[1] for r in refs]), "swa_32k")
+
+
+def test_config3_decode_1m():
+    _say("config 3")
+    wl = I.config_workload(3, device="cuda")
+    sel, out, lse = run_sparse_layer(wl)
+    _check_all(wl, sel, out, lse, range(wl.n_tok), what="decode_1m")
+
+
+def test_config4_prefill_chunk_sampled():
+    _say("config 4")
+    wl = I.config_workload(4, device="cuda")
+    sel, out, lse = run_sparse_layer(wl)
+    rng = np.random.default_rng(4)
+    sample = sorted(set(rng.choice(wl.n_tok, size=12, replace=False).tolist()) | {0, wl.n_tok - 1})
+    _check_all(wl, sel, out, lse, sample, what="prefill_chunk")
+
+
+def test_all_scores_tied_takes_lowest_blocks():
+    """Index query of zeros: every score is 0, so the first 512 blocks win. The
+    history (5000 blocks) also overflows the candidate list and exercises the
+    select-over-all-scores path."""
+    _say("all tied")
+    spec = I.WorkloadSpec("tied", batch=2, seq_lens=[40001, 5000], q_per_seq=2)
+    wl = I.make_workload(spec, seed=21, device="cuda")
+    wl.q_idx.zero_()
+    sel, out, lse = run_sparse_layer(wl)
+    sel_h = sel.cpu().numpy()
+    for t in range(wl.n_tok):
+        cb = int(wl.q_pos[t]) // 8
+        assert sel_h[t].tolist() == list(range(min(512, cb))) + [-1] * (512 - min(512, cb))
+    _check_all(wl, sel, out, lse, range(wl.n_tok), what="tied")
+
+
+def test_heavy_ties():
+    """Index inputs in {0, 1}: many blocks share the threshold score."""
+    _say("heavy ties")
+    spec = I.WorkloadSpec("ties01", batch=3, seq_lens=[20000, 33000, 70000], q_per_seq=2, idx_lo=0, idx_hi=1)
+    wl = I.make_workload(spec, seed=22, device="cuda")
+    sel, out, lse = run_sparse_layer(wl)
+    ov = OracleView(wl)
+    sel_h = sel.cpu().numpy()
+    for t in range(wl.n_tok):
+        assert sel_h[t].tolist() == ov.selection(t).tolist(), f"token {t}"
+
+
+def test_invalid_tokens_attend_nothing():
+    _say("invalid tokens")
+    spec = I.WorkloadSpec("inv", batch=2, seq_lens=[3000, 2000], q_per_seq=2)
+    wl = I.make_workload(spec, seed=23, device="cuda")
+    wl.q_seq[0] = -1           # sequence id out of range
+    wl.q_seq[1] = 2            # = batch
+    wl.q_pos[2] = 2000         # = seq_len of sequence 1
+    sel, out, lse = run_sparse_layer(wl)
+    for t in range(3):
+        assert (sel[t] == -1).all()
+        assert (out[t] == 0).all()
+        assert torch.isneginf(lse[t]).all()
+    _check_all(wl, sel, out, lse, [3], what="valid neighbour")
+
+
+def test_poison_unread_blocks_and_future_positions():
+    """NaN in every K/V block that is neither selected nor current, and in the
+    current block past the query position: outputs bit-identical."""
+    _say("poison")
+    spec = I.WorkloadSpec("poison", batch=2, seq_lens=[6001, 9003], q_per_seq=1)
+    wl = I.make_workload(spec, seed=24, device="cuda")
+    pt, sl, qs, qp = device_tables(wl)
+    sel, out, lse = run_sparse_layer(wl, tabs=(pt, sl, qs, qp))
+    sel_h = sel.cpu().numpy()
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device="cuda")
+    for t in range(wl.n_tok):
+        b, p = int(wl.q_seq[t]), int(wl.q_pos[t])
+        keep = set(int(x) for x in sel_h[t] if x >= 0) | {p // 8}
+        row = wl.page_table[b]
+        for blk in range((int(wl.seq_lens[b]) + 7) // 8):
+            if blk in keep:
+                continue
+            page = int(row[blk // 8])
+            wl.k_cache[page, :, blk % 8] = nan
+            wl.v_cache[page, :, blk % 8] = nan
+        # future positions inside the current block: positions p+1 .. 8*cb+7
+        cbk = p // 8
+        page = int(row[cbk // 8])
+        for pos in range(p + 1, 8 * cbk + 8):
+            for g in range(4):
+                I.pack_k_rows(wl.k_cache, row, [pos], g, torch.full((1, 192), float("nan")))
+                I.pack_v_rows(wl.v_cache, row, [pos], g, torch.full((1, 192), float("nan")))
+    from sparse_block_indexed_amd import ops
+    out2, lse2 = ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert torch.equal(lse, lse2)
+
+
+def test_deterministic_and_batch_invariant():
+    _say("determinism")
+    wl = I.config_workload(0, device="cuda", seed=31)
+    wl_big = I.make_workload(I.WorkloadSpec("bi", batch=5, seq_lens=[8192, 3000, 20000, 8192, 500], q_per_seq=1),
+                             seed=32, device="cuda")
+    # place config-0's sequence as sequence 3 of the bigger batch
+    b3 = wl_big.page_table[3]
+    wl_big.k_cache[torch.as_tensor(b3[:128].astype(np.int64), device="cuda")] = wl.k_cache[:128]
+    wl_big.v_cache[torch.as_tensor(b3[:128].astype(np.int64), device="cuda")] = wl.v_cache[:128]
+    wl_big.k_idx_cache[torch.as_tensor(b3[:128].astype(np.int64), device="cuda")] = wl.k_idx_cache[:128]
+    wl_big.q[3] = wl.q[0]
+    wl_big.q_idx[3] = wl.q_idx[0]
+    for S in (1, 8):
+        s1, o1, l1 = run_sparse_layer(wl, num_splits=S)
+        s2, o2, l2 = run_sparse_layer(wl, num_splits=S)
+        assert torch.equal(s1, s2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+        s3, o3, l3 = run_sparse_layer(wl_big, num_splits=S)
+        assert torch.equal(s1[0], s3[3]) and torch.equal(o1[0], o3[3]) and torch.equal(l1[0], l3[3])
+
+
+def test_split_count_changes_only_rounding():
+    _say("splits")
+    wl = I.config_workload(0, device="cuda", seed=33)
+    ref = None
+    for S in (1, 2, 5, 32, 64):
+        sel, out, lse = run_sparse_layer(wl, num_splits=S)
+        if ref is None:
+            ref = (out, lse)
+            continue
+        assert_close_outputs(bf16_to_np(out), lse.cpu().numpy(), bf16_to_np(ref[0]), ref[1].cpu().numpy(), f"S={S}")
+
+
+def test_page_permutation_invariance():
+    _say("page permutation")
+    spec = I.WorkloadSpec("perm", batch=2, seq_lens=[7000, 12345], q_per_seq=2)
+    wl = I.make_workload(spec, seed=34, device="cuda")
+    sel1, out1, lse1 = run_sparse_layer(wl, num_splits=2)
+    perm = np.random.default_rng(5).permutation(wl.num_pages)
+    inv = torch.as_tensor(np.argsort(perm).astype(np.int64), device="cuda")
+    # new physical page perm[i] holds old page i
+    wl.k_cache = wl.k_cache[inv].contiguous()
+    wl.v_cache = wl.v_cache[inv].contiguous()
+    wl.k_idx_cache = wl.k_idx_cache[inv].contiguous()
+    wl.page_table = np.where(wl.page_table >= 0, perm[np.maximum(wl.page_table, 0)], -1).astype(np.int32)
+    sel2, out2, lse2 = run_sparse_layer(wl, num_splits=2)
+    assert torch.equal(sel1, sel2) and torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_closed_forms_constant_v_and_zero_q():
+    _say("closed forms")
+    spec = I.WorkloadSpec("cf", batch=2, seq_lens=[5000, 777], q_per_seq=2)
+    wl = I.make_workload(spec, seed=35, device="cuda")
+    const = torch.randn(4, 192, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    # constant V per group: every (page, group, block) unit holds the group's row for all 8 tokens
+    v = const.to("cuda")[:, :, None].expand(4, 192, 8).reshape(4, 1536)
+    wl.v_cache[:] = v[None, :, None, :]
+    sel, out, lse = run_sparse_layer(wl)
+    for t in range(wl.n_tok):
+        for h in range(64):
+            assert torch.equal(out[t, h].float(), const[h // 16].float().cuda()), (t, h)
+    # Q = 0: uniform weights -> lse = ln(number of attended tokens)
+    wl.q.zero_()
+    sel, out, lse = run_sparse_layer(wl)
+    for t in range(wl.n_tok):
+        n = len(O.sparse_token_positions(sel[t].cpu().numpy(), int(wl.q_pos[t])))
+        assert torch.allclose(lse[t], torch.full_like(lse[t], math.log(n)), atol=1e-4)
+
+
+def test_merge_entry_point():
+    _say("merge")
+    from sparse_block_indexed_amd import ops
+    g = torch.Generator().manual_seed(7)
+    n_tok, S = 5, 6
+    po = torch.randn(n_tok, S, 64, 192, generator=g)
+    pl = torch.randn(n_tok, S, 64, generator=g) * 3
+    pl[0, 2:] = -float("inf")
+    pl[1, :] = -float("inf")
+    out, lse = ops.merge(po.cuda(), pl.cuda())
+    torch.cuda.synchronize()
+    for t in range(n_tok):
+        ro, rl = O.merge(po[t].double().numpy(), pl[t].double().numpy())
+        assert np.abs(bf16_to_np(out[t]) - ro).max() <= 2e-2
+        if t == 1:
+            assert (out[t] == 0).all() and torch.isneginf(lse[t]).all()
+        else:
+            assert np.abs(lse[t].cpu().numpy() - rl).max() <= 1e-4
+
+
+def test_zero_tokens_is_a_no_op():
+    from sparse_block_indexed_amd import ops
+    spec = I.WorkloadSpec("z", batch=1, seq_lens=[100], q_per_seq=1)
+    wl = I.make_workload(spec, seed=36, device="cuda")
+    pt, sl, _, _ = device_tables(wl)
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    sel = ops.indexer_topk(wl.q_idx[:0], wl.k_idx_cache, pt, sl, e, e, 512)
+    out, lse = ops.sparse_decode(wl.q[:0], wl.k_cache, wl.v_cache, pt, sl, e, e, sel, SCALE)
+    torch.cuda.synchronize()
+    assert sel.shape == (0, 512) and out.shape == (0, 64, 192)
