@@ -147,9 +147,12 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_d
   // is correct, a good one reads each key once).
   a.group_size = std::max(1, std::min(4, n_tok / pd.batch));
   const int ngroups = (n_tok + a.group_size - 1) / a.group_size;
+  // Few long workgroups: about two per CU (the score kernel's occupancy), so
+  // each workgroup's fixed start-up cost is paid about once per CU.
   int chunk = 4096;
-  while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < 512) chunk >>= 1;
   a.chunk_blocks = chunk;
+  a.bitmap_words = a.max_hist_blocks <= sa::kBitmapMaxBlocks ? (a.max_hist_blocks + 31) / 32 : 0;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
   a.cand_count = reinterpret_cast<uint32_t*>(ws + w.count_off);

@@ -60,6 +60,12 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// K/V blocks are read once per call: non-temporal loads keep them from
+// displacing reusable lines in L2 and the MALL.
+__device__ __forceinline__ u32x4 load16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <bool kWindow>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   __shared__ int32_t s_unit[kMaxSlots];
@@ -149,48 +155,48 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   u32x4 kr[2][6];
   u32x4 vr[12];
 
+  // Loads are branch-free so that the compiler's waits stay precise: a slot
+  // with nothing to read (padding, unreadable page) reads unit 0 instead, and
+  // its scores are masked to -inf and its V zeroed below.
   auto load_k = [&](int c) {
     const int slot = 4 * c + (lq >> 2);
-    const int unit = slot < n ? s_unit[slot] : -1;
-    if (unit >= 0) {
-      const uint8_t* pk = kbase + (size_t)unit * kUnitBytes;
+    const int unit = slot < n ? max(s_unit[slot], 0) : 0;
+    const uint8_t* pk = kbase + (size_t)unit * kUnitBytes;
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        kr[0][i] = load16(pk + i * 128);
-        kr[1][i] = load16(pk + i * 128 + 64);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) kr[0][i] = kr[1][i] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < 6; ++i) {
+      kr[0][i] = load16_stream(pk + i * 128);
+      kr[1][i] = load16_stream(pk + i * 128 + 64);
     }
   };
   auto load_v = [&](int c) {
     const int slot = 4 * c + lg;
-    const int unit = slot < n ? s_unit[slot] : -1;
-    if (unit >= 0) {
-      const uint8_t* pv = vbase + (size_t)unit * kUnitBytes;
+    const int unit = slot < n ? max(s_unit[slot], 0) : 0;
+    const uint8_t* pv = vbase + (size_t)unit * kUnitBytes;
 #pragma unroll
-      for (int i = 0; i < 12; ++i) vr[i] = load16(pv + i * 256);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 12; ++i) vr[i] = u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 12; ++i) vr[i] = load16_stream(pv + i * 256);
   };
 
+  // Chunks of this wave: wave, wave + 4, ... The next chunk's K is issued
+  // right after the score MFMAs and its V right after the PV MFMAs. The
+  // prefetch is unconditional (the last chunk re-reads itself, an L2 hit) so
+  // that every wait in the loop covers exactly the data it needs.
   int c = wave;
   if (c < nchunks) {
+    const int c_last = c + ((nchunks - 1 - c) / kWaves) * kWaves;
     load_k(c);
     load_v(c);
-  }
-  for (; c < nchunks; c += kWaves) {
+    for (;; c += kWaves) {
+    const int cn = min(c + kWaves, c_last);
     f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
       st0 = mfma_bf16(kr[0][i], qv[i], st0);
       st1 = mfma_bf16(kr[1][i], qv[i], st1);
     }
-    const int cn = c + kWaves;
-    if (cn < nchunks) load_k(cn);
+    // keep the refill below the MFMAs that read kr: hoisting it would need a
+    // second set of K registers
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(cn);
 
     // this lane's block (lg) of the chunk and its valid positions
     const int slot = 4 * c + lg;
@@ -225,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     }
     const u32x4 pb = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                       pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
-    // the row sum uses the same rounded probabilities the PV product sees, so
-    // the weights are normalised consistently
+    // the row sum that normalises O uses the same rounded probabilities the PV
+    // product sees; the unrounded sum gives lse
     float psum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
@@ -237,10 +243,11 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] *= alpha;
 
-    // Positions outside the attended range inside a loaded block (the current
-    // block past p, the window's first block before lo) may hold anything;
-    // zero their V so that 0-probability never meets a non-finite value.
-    if (__any(blk_ok && okmask != 0xffu)) {
+    // Positions outside the attended range (the current block past p, the
+    // window's first block before lo, slots that read unit 0 as a stand-in)
+    // may hold anything; zero their V so that a zero probability never meets a
+    // non-finite value.
+    if (__any(okmask != 0xffu)) {
       u32x4 vm;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -253,7 +260,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] = mfma_bf16(vr[i], pb, acc[i]);
-    if (cn < nchunks) load_v(cn);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(cn);
+    if (c == c_last) break;
+    }
   }
 
   // ---- merge the 4 wave states (fixed order) and write -------------------

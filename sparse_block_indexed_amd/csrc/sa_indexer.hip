@@ -12,8 +12,9 @@
 //  1. zero      clear the per-token histograms and candidate counters.
 //  2. score     stream every historical index key of a sequence once and score
 //               all of that sequence's query tokens against it (v_dot2 bf16 ->
-//               fp32); write fp32 scores and add each score to a 2048-bin
-//               histogram of the top 11 bits of its order-preserving key.
+//               fp32, eight lanes per key, DPP reduction); write fp32 scores
+//               and add each score to a 2048-bin histogram of the top 11 bits
+//               of its order-preserving key.
 //  3. collect   per (token, score chunk): find the histogram bin that holds the
 //               k-th largest score and append every score at or above that bin
 //               to a small per-token candidate list.
@@ -35,8 +36,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = 4;
+constexpr int kMaxChunkBlocks = 4096;   // the host never picks a larger score chunk
+constexpr int kFuseLimit = 16384;       // histories up to this many blocks select straight from their scores
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// index keys are read once per call
+__device__ __forceinline__ u32x4 load16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
 // -0 maps like +0.
@@ -65,8 +72,10 @@ __device__ __forceinline__ int hist_blocks(const IndexerArgs& a, int t, int* seq
 // block-wide helpers (256 threads = 4 waves)
 // ---------------------------------------------------------------------------
 
-// Exclusive suffix sum over the 256 threads: returns sum of v over threads > tid.
-__device__ uint32_t block_suffix_exclusive(uint32_t v, uint32_t* s_tmp /*[4]*/) {
+// Exclusive suffix sum over the NT threads of the block: the sum of v over
+// threads with a larger index. s_tmp holds NT / 64 words.
+template <int NT>
+__device__ uint32_t block_suffix_exclusive(uint32_t v, uint32_t* s_tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -77,13 +86,14 @@ __device__ uint32_t block_suffix_exclusive(uint32_t v, uint32_t* s_tmp /*[4]*/) 
   if (lane == 0) s_tmp[wave] = x;   // wave total
   __syncthreads();
   uint32_t above = 0;
-  for (int w = wave + 1; w < 4; ++w) above += s_tmp[w];
+  for (int w = wave + 1; w < NT / 64; ++w) above += s_tmp[w];
   __syncthreads();
   return above + x - v;
 }
 
-// Exclusive prefix sum over the 256 threads; *total receives the block total.
-__device__ uint32_t block_prefix_exclusive(uint32_t v, uint32_t* s_tmp /*[4]*/, uint32_t* total) {
+// Exclusive prefix sum over the NT threads; *total receives the block total.
+template <int NT>
+__device__ uint32_t block_prefix_exclusive(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -94,7 +104,7 @@ __device__ uint32_t block_prefix_exclusive(uint32_t v, uint32_t* s_tmp /*[4]*/, 
   if (lane == 63) s_tmp[wave] = x;
   __syncthreads();
   uint32_t below = 0, tot = 0;
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     if (w < wave) below += s_tmp[w];
     tot += s_tmp[w];
   }
@@ -105,18 +115,19 @@ __device__ uint32_t block_prefix_exclusive(uint32_t v, uint32_t* s_tmp /*[4]*/, 
 
 // Among bins h[0..nbins) (a higher bin holds larger keys), find the bin that
 // holds the k-th largest element: above < k <= above + h[bin], where above is
-// the count in higher bins. Needs sum(h) >= k >= 1 and nbins in {1024, 2048}.
+// the count in higher bins. Needs sum(h) >= k >= 1 and nbins a multiple of NT.
 // Result is broadcast through s_res[0] (bin) and s_res[1] (above).
+template <int NT>
 __device__ void select_bin(const uint32_t* h, int nbins, uint32_t k, uint32_t* s_tmp, uint32_t* s_res) {
   if (threadIdx.x == 0) {   // defined result even for inconsistent input
     s_res[0] = 0u;
     s_res[1] = 0u;
   }
-  const int per = nbins / kThreads;
+  const int per = nbins / NT;
   const int b0 = threadIdx.x * per;
   uint32_t part = 0;
   for (int i = 0; i < per; ++i) part += h[b0 + i];
-  uint32_t cum = block_suffix_exclusive(part, s_tmp);
+  uint32_t cum = block_suffix_exclusive<NT>(part, s_tmp);
   if (cum < k && cum + part >= k) {
     for (int i = per - 1; i >= 0; --i) {
       const uint32_t c = h[b0 + i];
@@ -131,6 +142,26 @@ __device__ void select_bin(const uint32_t* h, int nbins, uint32_t k, uint32_t* s
   __syncthreads();
 }
 
+// In-place bitonic sort of n (a power of two) values in LDS, by the NT threads.
+template <int NT, typename T, bool kDescending>
+__device__ void bitonic_sort(T* x, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (n >> 1); i += NT) {
+        const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));   // stride is a power of two
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0) != kDescending;   // this pair sorts ascending
+        const T a = x[lo], b = x[hi];
+        if ((a > b) == up) {
+          x[lo] = b;
+          x[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 1. zero
 // ---------------------------------------------------------------------------
@@ -142,68 +173,112 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // 2. score
 // ---------------------------------------------------------------------------
-// One pass over blocks [lo, hi) of sequence b for NQ query tokens. Four lanes
-// share one block key: lane quarter q4 reads 16-byte chunks 4i + q4 (i = 0..7),
-// so each quad reads 64 contiguous bytes per load and a wave covers 16 keys.
+// Sum over the 8 lanes of an aligned lane octet, with DPP moves (no LDS):
+// swap neighbours, swap pairs, then add the mirrored half-row. Every lane of
+// the octet ends with the same bits.
+__device__ __forceinline__ float octet_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return v;
+}
+
+// Score one step: 8 blocks per wave, 8 lanes per block key (lane q8 holds the
+// 16-byte chunks q8 + 8i, i = 0..3, of the key, so each load instruction reads
+// whole 128-byte lines).
 template <int NQ>
-__device__ void score_run(const IndexerArgs& a, int b, const int* tok, const int* hslot, const int* ncb,
-                          int lo, int hi, uint32_t (*s_hist)[kHistBins]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int q4 = lane & 3;
-  const int sub = lane >> 2;
-  u32x4 qv[NQ][8];
+__device__ __forceinline__ void score_step(const IndexerArgs& a, const int* tok, const int* hslot, const int* ncb,
+                                           const u32x4* s_q, const u32x4 (&kv)[4], int beta, bool in, bool ok,
+                                           int q8, uint32_t (*s_hist)[kHistBins]) {
+  // The queries are read from LDS at every step on purpose: held in registers
+  // they would take the VGPRs that keep key loads in flight. The empty asm
+  // makes the offset opaque so the reads are not hoisted out of the loop.
+  int qoff = q8;
+  asm volatile("" : "+v"(qoff));
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const uint8_t* qp = a.q_idx + (size_t)tok[j] * kKeyBytes + q4 * 16;
+    float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qv[j][i] = load16(qp + i * 64);
-  }
-  const int32_t* prow = a.page_table + (size_t)b * a.max_pages;
-  for (int base = lo + wave * 16; base < hi; base += 64) {
-    const int beta = base + sub;
-    const bool in = beta < hi;
-    const int page = in ? prow[beta >> 3] : -1;
-    const bool ok = in && page >= 0 && page < a.num_pages;
-    u32x4 kv[8];
-    if (ok) {
-      const uint8_t* kp = a.k_idx_cache + ((size_t)page * kBlocksPerPage + (beta & 7)) * kKeyBytes + q4 * 16;
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 q = s_q[j * (kKeyBytes / 16) + qoff + 8 * i];   // broadcast read
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kv[i] = load16(kp + i * 64);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kv[i] = u32x4{0, 0, 0, 0};
+      for (int w = 0; w < 4; ++w) s = dot2(kv[i][w], q[w], s);
     }
-    float acc[NQ];
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) s = dot2(kv[i][w], qv[j][i][w], s);
-      }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      acc[j] = ok ? s : -INFINITY;   // an unreadable page ranks last
-    }
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      if (in && q4 == (j & 3) && beta < ncb[j]) {
-        a.scores[(size_t)tok[j] * a.max_hist_blocks + beta] = acc[j];
-        atomicAdd(&s_hist[hslot[j]][score_key(acc[j]) >> 21], 1u);
-      }
+    s = octet_sum(s);
+    const float sc = ok ? s : -INFINITY;   // an unreadable page ranks last
+    if (in && q8 == j && beta < ncb[j]) {
+      a.scores[(size_t)tok[j] * a.max_hist_blocks + beta] = sc;
+      atomicAdd(&s_hist[hslot[j]][score_key(sc) >> 21], 1u);
     }
   }
 }
 
+// One pass over blocks [lo, hi) of one sequence for NQ of its query tokens.
+// The physical page of every block comes from s_pages (preloaded). Four steps
+// (16 KB per wave) are in flight: after a step is scored its buffer is refilled
+// with the step four ahead. Refills are unconditional (a step past hi reads the
+// cache's first key and stores nothing), so each wait leaves the other three
+// buffers' loads in flight.
+template <int NQ>
+__device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot, const int* ncb, int lo, int hi,
+                          const int32_t* s_pages, const u32x4* s_q, uint32_t (*s_hist)[kHistBins]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q8 = lane & 7;
+  const int sub = lane >> 3;
+  const int page0 = lo >> 3;
+  auto locate = [&](int beta, bool& in, bool& ok) -> const uint8_t* {
+    in = beta < hi;
+    const int page = in ? s_pages[(beta >> 3) - page0] : -1;
+    ok = in && page >= 0 && page < a.num_pages;
+    const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * kKeyBytes : 0;
+    return a.k_idx_cache + off + q8 * 16;
+  };
+  // steps of this wave: 8 blocks each, starting at lo + 8 * wave, stride 32
+  const int first = lo + wave * 8;
+  const int nsteps = first < hi ? (hi - first + 31) / 32 : 0;
+  if (nsteps == 0) return;
+  u32x4 k0[4], k1[4], k2[4], k3[4];
+  bool in0, ok0, in1, ok1, in2, ok2, in3, ok3;
+  int b0 = first + sub, b1 = b0 + 32, b2 = b0 + 64, b3 = b0 + 96;
+  auto fill = [&](u32x4 (&kv)[4], int beta, bool& in, bool& ok) {
+    const uint8_t* p = locate(beta, in, ok);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kv[i] = load16_stream(p + i * 128);
+  };
+  fill(k0, b0, in0, ok0);
+  fill(k1, b1, in1, ok1);
+  fill(k2, b2, in2, ok2);
+  fill(k3, b3, in3, ok3);
+  for (int st = 0; st < nsteps; st += 4) {
+    score_step<NQ>(a, tok, hslot, ncb, s_q, k0, b0, in0, ok0, q8, s_hist);
+    b0 += 128;
+    fill(k0, b0, in0, ok0);
+    score_step<NQ>(a, tok, hslot, ncb, s_q, k1, b1, in1, ok1, q8, s_hist);
+    b1 += 128;
+    fill(k1, b1, in1, ok1);
+    score_step<NQ>(a, tok, hslot, ncb, s_q, k2, b2, in2, ok2, q8, s_hist);
+    b2 += 128;
+    fill(k2, b2, in2, ok2);
+    score_step<NQ>(a, tok, hslot, ncb, s_q, k3, b3, in3, ok3, q8, s_hist);
+    b3 += 128;
+    fill(k3, b3, in3, ok3);
+  }
+}
+
+// Runs of up to GS query tokens of one sequence share a pass over its keys; GS
+// is the host's group size, so a one-token decode does not pay for four query
+// register sets.
+template <int GS>
 __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
-  __shared__ uint32_t s_hist[kMaxGroup][kHistBins];
+  __shared__ uint32_t s_hist[GS][kHistBins];
+  __shared__ int32_t s_pages[kMaxChunkBlocks / kBlocksPerPage + 1];
+  __shared__ u32x4 s_q[GS * (kKeyBytes / 16)];   // index queries of the current run
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const int chunk = blockIdx.x % nchunk;
   const int grp = blockIdx.x / nchunk;
-  const int t0 = grp * a.group_size;
-  const int ng = min(a.group_size, a.n_tok - t0);
+  const int t0 = grp * GS;
+  const int ng = min(GS, a.n_tok - t0);
   int seq[kMaxGroup], ncb[kMaxGroup];
   for (int j = 0; j < kMaxGroup; ++j) {
     ncb[j] = 0;
@@ -235,13 +310,19 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
         }
       }
     }
-    switch (nq) {
-      case 1: score_run<1>(a, seq[j0], tok, hslot, cbs, lo, hi, s_hist); break;
-      case 2: score_run<2>(a, seq[j0], tok, hslot, cbs, lo, hi, s_hist); break;
-      case 3: score_run<3>(a, seq[j0], tok, hslot, cbs, lo, hi, s_hist); break;
-      case 4: score_run<4>(a, seq[j0], tok, hslot, cbs, lo, hi, s_hist); break;
-      default: break;
-    }
+    if (nq == 0) continue;
+    // physical pages of blocks [lo, hi) of this sequence
+    const int32_t* prow = a.page_table + (size_t)seq[j0] * a.max_pages;
+    const int np = ((hi - 1) >> 3) - (lo >> 3) + 1;
+    __syncthreads();   // the previous run is done with s_pages
+    for (int i = threadIdx.x; i < np; i += kThreads) s_pages[i] = prow[(lo >> 3) + i];
+    for (int i = threadIdx.x; i < nq * (kKeyBytes / 16); i += kThreads)
+      s_q[i] = load16(a.q_idx + (size_t)tok[i / (kKeyBytes / 16)] * kKeyBytes + (i % (kKeyBytes / 16)) * 16);
+    __syncthreads();
+    if (nq == 1) score_run<1>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist);
+    if constexpr (GS >= 2) { if (nq == 2) score_run<2>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if constexpr (GS >= 3) { if (nq == 3) score_run<3>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if constexpr (GS >= 4) { if (nq == 4) score_run<4>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) {
@@ -254,92 +335,81 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
 // 3. collect
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void collect_kernel(IndexerArgs a) {
+  constexpr int kPer = kCollectChunk / kThreads;
   __shared__ uint32_t s_h[kHistBins];
   __shared__ uint32_t s_tmp[4];
   __shared__ uint32_t s_res[2];
+  __shared__ uint32_t s_base;
   const int nck = (a.max_hist_blocks + kCollectChunk - 1) / kCollectChunk;
   const int ck = blockIdx.x % nck;
   const int t = blockIdx.x / nck;
   int b;
   const int ncand = min(hist_blocks(a, t, &b), a.max_hist_blocks);
   const int lo = ck * kCollectChunk;
-  if (ncand <= a.topk || lo >= ncand) return;
+  if (ncand <= kFuseLimit || lo >= ncand) return;   // short histories select in finalize
   const int hi = min(ncand, lo + kCollectChunk);
+  // issue every load first: this chunk's scores (coalesced) and the histogram
+  const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+  float sv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int beta = lo + j * kThreads + (int)threadIdx.x;
+    sv[j] = beta < hi ? srow[beta] : 0.f;
+  }
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_h[i] = a.hist[(size_t)t * kHistBins + i];
   __syncthreads();
-  select_bin(s_h, kHistBins, (uint32_t)a.topk, s_tmp, s_res);
+  select_bin<kThreads>(s_h, kHistBins, (uint32_t)a.topk, s_tmp, s_res);
   const uint32_t b1 = s_res[0];
-
-  const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+  uint32_t takes = 0, cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int beta = lo + j * kThreads + (int)threadIdx.x;
+    const bool take = beta < hi && (score_key(sv[j]) >> 21) >= b1;
+    takes |= take ? (1u << j) : 0u;
+    cnt += take ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t off = block_prefix_exclusive<kThreads>(cnt, s_tmp, &total);
+  if (total == 0) return;
+  if (threadIdx.x == 0) s_base = atomicAdd(&a.cand_count[t], total);
+  __syncthreads();
+  uint32_t pos = s_base + off;
   uint2* crow = a.cand + (size_t)t * kCandCap;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int base = lo + wave * 64; base < hi; base += kThreads) {
-    const int beta = base + lane;
-    uint32_t key = 0;
-    bool take = false;
-    if (beta < hi) {
-      key = score_key(srow[beta]);
-      take = (key >> 21) >= b1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if ((takes >> j) & 1u) {
+      if (pos < (uint32_t)kCandCap)
+        crow[pos] = make_uint2(score_key(sv[j]), (uint32_t)(lo + j * kThreads + (int)threadIdx.x));
+      ++pos;
     }
-    const uint64_t m = __ballot(take);
-    if (m == 0) continue;
-    uint32_t basepos = 0;
-    if (lane == 0) basepos = atomicAdd(&a.cand_count[t], (uint32_t)__popcll(m));
-    basepos = __shfl(basepos, 0);
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (take && basepos + rank < (uint32_t)kCandCap) crow[basepos + rank] = make_uint2(key, (uint32_t)beta);
   }
 }
 
 // ---------------------------------------------------------------------------
 // 4. finalize
 // ---------------------------------------------------------------------------
+constexpr int kFinalThreads = 512;
+
+constexpr int kTieCap = 2048;   // threshold-bin entries resolved in LDS
+
 struct FinalizeLds {
-  uint32_t key[kCandCap];
-  uint32_t idx[kCandCap];
+  uint32_t tzk[kTieCap];    // keys of the threshold bin
+  uint32_t tzi[kTieCap];    // their block ids
   uint32_t h[kHistBins];
-  int32_t sel[SA_MAX_TOPK];
-  uint32_t tmp[4];
+  uint32_t tmp[kFinalThreads / 64];
   uint32_t res[2];
-  uint32_t n_gt;
-  uint32_t n_eq;
+  uint32_t n_tz;
 };
 
-// Exact k-th largest key over the keys held in LDS (n of them): three radix
-// levels. Returns tau; *count_gt receives how many keys are strictly larger.
-__device__ uint32_t radix_kth_lds(FinalizeLds& s, int n, uint32_t k, uint32_t* count_gt) {
-  uint32_t prefix = 0, above = 0;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int lvl = 0; lvl < 3; ++lvl) {
-    const int sh = shifts[lvl];
-    const int nb = 1 << widths[lvl];
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) s.h[i] = 0u;
-    __syncthreads();
-    const int hs = sh + widths[lvl];   // bits above this digit must match the prefix
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const uint32_t key = s.key[i];
-      const bool match = hs >= 32 || (key >> hs) == (prefix >> hs);
-      if (match) atomicAdd(&s.h[(key >> sh) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    select_bin(s.h, nb, k - above, s.tmp, s.res);
-    prefix |= s.res[0] << sh;
-    above += s.res[1];
-    __syncthreads();
-  }
-  *count_gt = above;
-  return prefix;
-}
-
-// Same radix select over all scores of a token in global memory (fallback for
-// candidate-list overflow); level 1 uses the histogram built by the score pass.
+// Exact k-th largest key over all of a token's scores (three radix levels, the
+// first from the score pass's histogram); *count_gt receives how many keys are
+// strictly larger.
 __device__ uint32_t radix_kth_global(const IndexerArgs& a, FinalizeLds& s, int t, int ncand, uint32_t k,
                                      uint32_t* count_gt) {
   const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
+  for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
   __syncthreads();
-  select_bin(s.h, kHistBins, k, s.tmp, s.res);
+  select_bin<kFinalThreads>(s.h, kHistBins, k, s.tmp, s.res);
   uint32_t prefix = s.res[0] << 21;
   uint32_t above = s.res[1];
   __syncthreads();
@@ -349,14 +419,14 @@ __device__ uint32_t radix_kth_global(const IndexerArgs& a, FinalizeLds& s, int t
     const int sh = shifts[lvl];
     const int nb = 1 << widths[lvl];
     const int hs = sh + widths[lvl];
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) s.h[i] = 0u;
+    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < ncand; i += kThreads) {
+    for (int i = threadIdx.x; i < ncand; i += kFinalThreads) {
       const uint32_t key = score_key(srow[i]);
       if ((key >> hs) == (prefix >> hs)) atomicAdd(&s.h[(key >> sh) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    select_bin(s.h, nb, k - above, s.tmp, s.res);
+    select_bin<kFinalThreads>(s.h, nb, k - above, s.tmp, s.res);
     prefix |= s.res[0] << sh;
     above += s.res[1];
     __syncthreads();
@@ -365,91 +435,179 @@ __device__ uint32_t radix_kth_global(const IndexerArgs& a, FinalizeLds& s, int t
   return prefix;
 }
 
-__global__ __launch_bounds__(kThreads) void finalize_kernel(IndexerArgs a) {
+// Selection over all scores in one ordered pass (used when the threshold bin
+// or the candidate list overflows, or the history is too long for the LDS
+// bitmaps): keys above tau, then keys equal to tau in block order until k are
+// taken; the output comes out ascending.
+__device__ void select_ordered_global(const IndexerArgs& a, FinalizeLds& s, int t, int ncand, int32_t* out) {
+  const int k = a.topk;
+  uint32_t count_gt;
+  const uint32_t tau = radix_kth_global(a, s, t, ncand, (uint32_t)k, &count_gt);
+  count_gt = min(count_gt, (uint32_t)k);
+  const uint32_t need_eq = (uint32_t)k - count_gt;
+  const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+  uint32_t eq_before = 0, sel_before = 0;
+  for (int base = 0; base < ncand; base += kFinalThreads) {
+    const int beta = base + threadIdx.x;
+    uint32_t key = 0;
+    if (beta < ncand) key = score_key(srow[beta]);
+    const bool gt = beta < ncand && key > tau;
+    const bool eq = beta < ncand && key == tau;
+    uint32_t eq_tot, sel_tot;
+    const uint32_t eq_rank = eq_before + block_prefix_exclusive<kFinalThreads>(eq ? 1u : 0u, s.tmp, &eq_tot);
+    const bool take = gt || (eq && eq_rank < need_eq);
+    const uint32_t pos = sel_before + block_prefix_exclusive<kFinalThreads>(take ? 1u : 0u, s.tmp, &sel_tot);
+    if (take && pos < (uint32_t)k) out[pos] = beta;
+    eq_before += eq_tot;
+    sel_before += sel_tot;
+  }
+}
+
+// Per token. The histogram bin b1 that holds the k-th largest score splits the
+// scores into "surely chosen" (bin above b1; fewer than k) and the threshold
+// bin. Two more radix levels over the threshold bin's keys give the exact k-th
+// key tau; keys above tau are chosen, and keys equal to tau are chosen in block
+// order until k are taken (a bitmap walk). The chosen ids are written ascending
+// by walking the selection bitmap. Short histories read their scores directly,
+// long ones the candidates gathered by collect_kernel.
+__global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) {
   __shared__ FinalizeLds s;
+  extern __shared__ uint32_t s_bm[];   // [2][bitmap_words]: chosen ids, ids tied at tau
   const int t = blockIdx.x;
   const int k = a.topk;
   int b;
   const int ncand = min(hist_blocks(a, t, &b), a.max_hist_blocks);
   int32_t* out = a.sel_idx + (size_t)t * k;
   if (ncand <= k) {
-    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < ncand ? i : -1;
+    for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = i < ncand ? i : -1;
     return;
   }
-  const uint32_t n = a.cand_count[t];
-  if (n > (uint32_t)kCandCap) {
-    // Overflow: radix select over every score, then an ordered compaction.
-    uint32_t count_gt;
-    const uint32_t tau = radix_kth_global(a, s, t, ncand, (uint32_t)k, &count_gt);
-    count_gt = min(count_gt, (uint32_t)k);
-    const uint32_t need_eq = (uint32_t)k - count_gt;
+  const int nw = (ncand + 31) >> 5;                 // bitmap words this token needs
+  uint32_t* sel_bm = s_bm;
+  uint32_t* eq_bm = s_bm + a.bitmap_words;
+  for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
+  if (nw <= a.bitmap_words) {
+    for (int i = threadIdx.x; i < nw; i += kFinalThreads) {
+      sel_bm[i] = 0u;
+      eq_bm[i] = 0u;
+    }
+  }
+  if (threadIdx.x == 0) s.n_tz = 0;
+  __syncthreads();
+  select_bin<kFinalThreads>(s.h, kHistBins, (uint32_t)k, s.tmp, s.res);
+  const uint32_t b1 = s.res[0];
+  const uint32_t above = min(s.res[1], (uint32_t)k - 1u);
+  const uint32_t in_bin = s.h[b1];
+  const bool fused = ncand <= kFuseLimit;
+  const uint32_t n_listed = fused ? 0u : a.cand_count[t];
+  if (nw > a.bitmap_words || in_bin > (uint32_t)kTieCap || (!fused && n_listed > (uint32_t)kCandCap)) {
+    select_ordered_global(a, s, t, ncand, out);
+    return;
+  }
+  auto classify = [&](uint32_t key, uint32_t beta) {
+    const uint32_t bin = key >> 21;
+    if (bin > b1) {
+      atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
+    } else if (bin == b1) {
+      const uint32_t slot = atomicAdd(&s.n_tz, 1u);
+      if (slot < (uint32_t)kTieCap) {
+        s.tzk[slot] = key;
+        s.tzi[slot] = beta;
+      }
+    }
+  };
+  if (fused) {
     const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
-    uint32_t eq_before = 0, sel_before = 0;
-    for (int base = 0; base < ncand; base += kThreads) {
-      const int beta = base + threadIdx.x;
-      uint32_t key = 0;
-      if (beta < ncand) key = score_key(srow[beta]);
-      const bool gt = beta < ncand && key > tau;
-      const bool eq = beta < ncand && key == tau;
-      uint32_t eq_tot, sel_tot;
-      const uint32_t eq_rank = eq_before + block_prefix_exclusive(eq ? 1u : 0u, s.tmp, &eq_tot);
-      const bool take = gt || (eq && eq_rank < need_eq);
-      const uint32_t pos = sel_before + block_prefix_exclusive(take ? 1u : 0u, s.tmp, &sel_tot);
-      if (take && pos < (uint32_t)k) out[pos] = beta;
-      eq_before += eq_tot;
-      sel_before += sel_tot;
+    constexpr int kPer = kFuseLimit / kFinalThreads;
+    float sv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int beta = j * kFinalThreads + (int)threadIdx.x;
+      sv[j] = beta < ncand ? srow[beta] : 0.f;
     }
-    return;
-  }
-  for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
-    const uint2 c = a.cand[(size_t)t * kCandCap + i];
-    s.key[i] = c.x;
-    s.idx[i] = c.y;
-  }
-  if (threadIdx.x == 0) {
-    s.n_gt = 0;
-    s.n_eq = 0;
-  }
-  __syncthreads();
-  uint32_t count_gt;
-  const uint32_t tau = radix_kth_lds(s, (int)n, (uint32_t)k, &count_gt);
-  count_gt = min(count_gt, (uint32_t)k);
-  const uint32_t need_eq = (uint32_t)k - count_gt;
-  // Keys above tau are all chosen; keys equal to tau are parked in h[] (reused)
-  for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
-    const uint32_t key = s.key[i];
-    if (key > tau) {
-      const uint32_t slot = atomicAdd(&s.n_gt, 1u);
-      if (slot < (uint32_t)SA_MAX_TOPK) s.sel[slot] = (int32_t)s.idx[i];
-    }
-    else if (key == tau) s.h[atomicAdd(&s.n_eq, 1u) % kHistBins] = s.idx[i];
-  }
-  __syncthreads();
-  const uint32_t n_eq = s.n_eq;
-  if (n_eq <= (uint32_t)kHistBins) {
-    for (uint32_t i = threadIdx.x; i < n_eq; i += kThreads) {
-      const uint32_t me = s.h[i];
-      uint32_t rank = 0;
-      for (uint32_t j = 0; j < n_eq; ++j) rank += s.h[j] < me ? 1u : 0u;
-      if (rank < need_eq) s.sel[count_gt + rank] = (int32_t)me;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int beta = j * kFinalThreads + (int)threadIdx.x;
+      if (beta < ncand) classify(score_key(sv[j]), (uint32_t)beta);
     }
   } else {
-    // more ties than the parking space: rank them straight from the candidate list
-    for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
-      if (s.key[i] != tau) continue;
-      const uint32_t me = s.idx[i];
-      uint32_t rank = 0;
-      for (uint32_t j = 0; j < n; ++j) rank += (s.key[j] == tau && s.idx[j] < me) ? 1u : 0u;
-      if (rank < need_eq) s.sel[count_gt + rank] = (int32_t)me;
+    for (uint32_t i = threadIdx.x; i < n_listed; i += kFinalThreads) {
+      const uint2 c = a.cand[(size_t)t * kCandCap + i];
+      classify(c.x, c.y);
     }
   }
   __syncthreads();
-  // chosen ids are distinct: their rank among themselves is their output slot
-  for (int i = threadIdx.x; i < k; i += kThreads) {
-    const int32_t me = s.sel[i];
-    int r = 0;
-    for (int j = 0; j < k; ++j) r += s.sel[j] < me ? 1 : 0;
-    out[r] = me;
+  // exact k-th key inside the threshold bin: two more radix levels
+  const int m = (int)min(s.n_tz, (uint32_t)kTieCap);
+  const uint32_t need = (uint32_t)k - above;
+  uint32_t prefix = b1 << 21;
+  uint32_t gt_in_bin = 0;
+  {
+    const int shifts[2] = {10, 0};
+    const int widths[2] = {11, 10};
+    for (int lvl = 0; lvl < 2; ++lvl) {
+      const int sh = shifts[lvl];
+      const int nb = 1 << widths[lvl];
+      const int hs = sh + widths[lvl];
+      for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
+      __syncthreads();
+      for (int i = threadIdx.x; i < m; i += kFinalThreads) {
+        const uint32_t key = s.tzk[i];
+        if ((key >> hs) == (prefix >> hs)) atomicAdd(&s.h[(key >> sh) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      select_bin<kFinalThreads>(s.h, nb, need - gt_in_bin, s.tmp, s.res);
+      prefix |= s.res[0] << sh;
+      gt_in_bin += s.res[1];
+      __syncthreads();
+    }
+  }
+  const uint32_t tau = prefix;
+  const uint32_t need_eq = need - min(gt_in_bin, need);
+  for (int i = threadIdx.x; i < m; i += kFinalThreads) {
+    const uint32_t key = s.tzk[i], beta = s.tzi[i];
+    if (key > tau) atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
+    else if (key == tau) atomicOr(&eq_bm[beta >> 5], 1u << (beta & 31));
+  }
+  __syncthreads();
+  // contiguous word range of this thread
+  const int per = (nw + kFinalThreads - 1) / kFinalThreads;
+  const int w0 = min(nw, (int)threadIdx.x * per), w1 = min(nw, w0 + per);
+  // ties at tau: the first need_eq in block order
+  {
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(eq_bm[w]);
+    uint32_t tot;
+    uint32_t before = block_prefix_exclusive<kFinalThreads>(cnt, s.tmp, &tot);
+    for (int w = w0; w < w1 && before < need_eq; ++w) {
+      uint32_t bits = eq_bm[w];
+      uint32_t take = 0;
+      while (bits != 0u && before < need_eq) {
+        const uint32_t low = bits & (0u - bits);
+        take |= low;
+        bits ^= low;
+        ++before;
+      }
+      if (take) sel_bm[w] |= take;   // this thread owns word w
+    }
+  }
+  __syncthreads();
+  // ascending output
+  {
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(sel_bm[w]);
+    uint32_t tot;
+    uint32_t pos = block_prefix_exclusive<kFinalThreads>(cnt, s.tmp, &tot);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = sel_bm[w];
+      while (bits != 0u) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (pos < (uint32_t)k) out[pos] = (int32_t)(w * 32 + bit);
+        ++pos;
+      }
+    }
+    for (uint32_t i = tot + threadIdx.x; i < (uint32_t)k; i += kFinalThreads) out[i] = -1;   // only if inconsistent
   }
 }
 
@@ -470,18 +628,24 @@ IndexerWorkspace indexer_workspace_layout(int n_tok, int max_pages_per_seq) {
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
   if (a.n_tok == 0) return hipSuccess;
-  const size_t nzero = (size_t)a.n_tok * kHistBins + (size_t)a.n_tok;   // hist then counters (adjacent)
-  const unsigned zblocks = (unsigned)std::min<size_t>((nzero + 1023) / 1024, 4096);
-  // hist and counters are contiguous only up to the padding of the hist region;
-  // clear them separately to stay exact.
-  zero_kernel<<<zblocks, 1024, 0, stream>>>(a.hist, (size_t)a.n_tok * kHistBins);
-  zero_kernel<<<1, 1024, 0, stream>>>(a.cand_count, (size_t)a.n_tok);
+  // histograms and candidate counters sit next to each other in the workspace
+  const size_t nzero = (reinterpret_cast<const uint8_t*>(a.scores) - reinterpret_cast<const uint8_t*>(a.hist)) / 4;
+  const unsigned zblocks = (unsigned)std::min<size_t>((nzero + 1023) / 1024, 2048);
+  zero_kernel<<<zblocks, 1024, 0, stream>>>(a.hist, nzero);
   const int ngroups = (a.n_tok + a.group_size - 1) / a.group_size;
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
-  score_kernel<<<dim3((unsigned)((long long)ngroups * nchunk)), dim3(kThreads), 0, stream>>>(a);
-  const int nck = (a.max_hist_blocks + kCollectChunk - 1) / kCollectChunk;
-  collect_kernel<<<dim3((unsigned)((long long)a.n_tok * nck)), dim3(kThreads), 0, stream>>>(a);
-  finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kThreads), 0, stream>>>(a);
+  const dim3 sgrid((unsigned)((long long)ngroups * nchunk));
+  switch (a.group_size) {
+    case 1: score_kernel<1><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
+    case 2: score_kernel<2><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
+    case 3: score_kernel<3><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
+    default: score_kernel<4><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
+  }
+  if (a.max_hist_blocks > kFuseLimit) {
+    const int nck = (a.max_hist_blocks + kCollectChunk - 1) / kCollectChunk;
+    collect_kernel<<<dim3((unsigned)((long long)a.n_tok * nck)), dim3(kThreads), 0, stream>>>(a);
+  }
+  finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ constexpr int kKeyBytes = kIdxDim * 2;                     // one index key
 constexpr int kHistBins = 2048;       // first radix digit: key bits 31..21
 constexpr int kCandCap = 4096;        // candidates kept per token for the in-LDS finish
 constexpr int kCollectChunk = 4096;   // scores per collect workgroup
+constexpr int kBitmapMaxBlocks = 1 << 17;   // longest history the finalize bitmaps cover (2 x 16 KB LDS)
 
 struct AttnArgs {
   const uint8_t* q;
@@ -63,6 +64,7 @@ struct IndexerArgs {
   int max_hist_blocks;      // max_pages * 8: stride of the score rows
   int group_size;           // query tokens scored per pass over a sequence's keys
   int chunk_blocks;         // blocks per score workgroup
+  int bitmap_words;         // LDS bitmap words per finalize workgroup (0: ordered select over all scores)
   int32_t* sel_idx;
   uint32_t* hist;           // [n_tok][kHistBins]
   uint32_t* cand_count;     // [n_tok]
