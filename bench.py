@@ -8,6 +8,11 @@ last 4 positions of each as query tokens (256 tokens), bf16 paged KV with
 randomly permuted 64-token pages, integer index inputs in [-4, 4], Q/K/V ~ N(0,1).
 Inputs are resident in HBM before timing starts.
 
+`--workload N` runs one of the other workloads instead (0: decode at 8K,
+batch 1; 2: sliding-window decode at 16K-32K, batch 64; 3: decode at 1M,
+batch 4; 4: a 16,384-token prefill chunk after 112K tokens); the default is
+the headline workload 1.
+
 Prints one JSON line. `value` is query tokens per second of the whole step.
 The roofline object covers the dominant kernel (the attention kernel): its
 algorithmic bytes (distinct K/V blocks read + Q + O + selection + lse) divided by
@@ -31,6 +36,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-attn decode query-tokens/s at 128K ctx, batch 64; achieved HBM GB/s"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 SCALE = 1.0 / math.sqrt(192.0)
 PMC_FILE = os.path.join(ROOT, "profiles", "attention_mtp_verify_128k_pmc.json")
 KERNEL_SOURCE = os.path.join(ROOT, "sparse_block_indexed_amd", "csrc", "sa_attention.hip")
@@ -54,9 +60,9 @@ def counter_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, sel_host, budget_s: float = 20.0, max_tokens: int = 64):
+def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: int = 64):
     """The fp64 oracle timed on this host over a bounded sample of the same
-    workload: whole sequences' verify tokens, until the budget is spent."""
+    workload: whole sequences' query tokens, until the budget is spent."""
     import torch
     from oracle import sa_oracle as O
     from sparse_block_indexed_amd import inputs as I
@@ -67,19 +73,26 @@ def cpu_baseline(wl, sel_host, budget_s: float = 20.0, max_tokens: int = 64):
         threads = 1
     done, t_cpu = 0, 0.0
     seqs_done = 0
+    dev = wl.k_cache.device
     for b in range(wl.batch):
-        toks = [t for t in range(wl.n_tok) if int(wl.q_seq[t]) == b]
+        toks = [t for t in range(wl.n_tok) if int(wl.q_seq[t]) == b][:max_tokens]
+        if not toks:
+            continue
         row = wl.page_table[b]
         # host copies of what the oracle reads (not timed): the sequence's index
         # keys and the pages of every attended block
         max_cb = max(int(wl.q_pos[t]) // 8 for t in toks)
         npg = (max_cb + 7) // 8
-        dev = wl.k_idx_cache.device
-        kidx = I.bf16_bits(wl.k_idx_cache.index_select(0, torch.as_tensor(row[:npg].astype(np.int64), device=dev)))
+        kidx = None
+        if window is None:
+            kidx = I.bf16_bits(wl.k_idx_cache.index_select(0, torch.as_tensor(row[:npg].astype(np.int64), device=dev)))
         pages = set()
         for t in toks:
             p = int(wl.q_pos[t])
-            pages |= {int(x) // 8 for x in sel_host[t] if x >= 0} | {p // 64}
+            if window is None:
+                pages |= {int(x) // 8 for x in sel_host[t] if x >= 0} | {p // 64}
+            else:
+                pages |= set(range(max(0, p - window + 1) // 64, p // 64 + 1))
         logical = np.array(sorted(pages), dtype=np.int64)
         idx = torch.as_tensor(row[logical].astype(np.int64), device=dev)
         kc, vc = I.bf16_bits(wl.k_cache.index_select(0, idx)), I.bf16_bits(wl.v_cache.index_select(0, idx))
@@ -90,17 +103,23 @@ def cpu_baseline(wl, sel_host, budget_s: float = 20.0, max_tokens: int = 64):
         t0 = time.perf_counter()
         for j, t in enumerate(toks):
             p = int(wl.q_pos[t])
-            keys = O.index_keys(kidx, np.arange(npg), p // 8)
-            sel = O.indexer_topk_token(O.bf16_to_f64(qib[j]), keys, 512)
-            O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.sparse_token_positions(sel, p), SCALE)
+            if window is None:
+                keys = O.index_keys(kidx, np.arange(npg), p // 8)
+                sel = O.indexer_topk_token(O.bf16_to_f64(qib[j]), keys, 512)
+                pos = O.sparse_token_positions(sel, p)
+            else:
+                pos = O.window_positions(p, window)
+            O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, pos, SCALE)
+            done += 1
+            if time.perf_counter() - t0 + t_cpu >= budget_s:
+                break
         t_cpu += time.perf_counter() - t0
-        done += len(toks)
         seqs_done += 1
         if t_cpu >= budget_s or done >= max_tokens:
             break
     return {"value": done / t_cpu, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} verify tokens ({seqs_done} sequences) of the 128K batch, fp64 numpy oracle, "
-                      f"{t_cpu:.1f} s of CPU time, host copies excluded"}
+            "sample": f"{done} query tokens ({seqs_done} sequences) of the {wl.spec.name} workload, fp64 numpy "
+                      f"oracle, {t_cpu:.1f} s of CPU time, host copies excluded"}
 
 
 def main():
@@ -111,6 +130,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after a 1 GiB write that evicts L2/MALL (reported separately)")
+    ap.add_argument("--workload", type=int, default=1, choices=range(5),
+                    help="0 decode 8K b1, 1 MTP verify 128K b64 (default), 2 SWA 32K b64, 3 decode 1M b4, "
+                         "4 prefill chunk 16K after 112K")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
     args = ap.parse_args()
@@ -138,13 +160,17 @@ def main():
     from sparse_block_indexed_amd import ops
 
     ops.load_library()
-    wl = I.config_workload(1, device=dev)
+    W = args.workload
+    wl = I.config_workload(W, device=dev)
     pt, sl, qs, qp = wl.device_ints(dev)
     topk = 512
+    window = 512 if W == 2 else None
     n_tok = wl.n_tok
-    S = ops.resolve_num_splits(n_tok, topk + 1, 0)
+    max_blocks = (window // 8 + 2) if window else topk + 1
+    S = ops.resolve_num_splits(n_tok, max_blocks, 0)
     sel = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
-    ws = torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk), dtype=torch.uint8, device=dev)
+    ws = None if window else torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk),
+                                         dtype=torch.uint8, device=dev)
     out = torch.empty((n_tok, 64, 192), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((n_tok, 64), dtype=torch.float32, device=dev)
     part_o = torch.empty((n_tok, S, 64, 192), dtype=torch.float32, device=dev) if S > 1 else None
@@ -154,11 +180,16 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
+        if window is None:
+            ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
-        ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=0, out=out,
-                          out_lse=lse, part_o=part_o, part_lse=part_lse)
+        if window is None:
+            ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=0, out=out,
+                              out_lse=lse, part_o=part_o, part_lse=part_lse)
+        else:
+            ops.swa_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, window, SCALE, num_splits=0, out=out,
+                           out_lse=lse, part_o=part_o, part_lse=part_lse)
         if ev is not None:
             ev[2].record(stream)
 
@@ -191,13 +222,29 @@ def main():
         cold_attn_ms = float(np.mean([c[1] for c in cold]))
         del flush
 
-    sel_host = sel.cpu().numpy()
-    attn_bytes = B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host)
-    idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk)
-    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = counter_traffic()
+    sel_host = sel.cpu().numpy() if window is None else None
+    if window is None:
+        attn_bytes = B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host)
+        idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk)
+        attn_flops = B.sparse_attention_flops(wl.q_pos, sel_host)
+        idx_flops = B.indexer_flops(wl.q_pos)
+    else:
+        attn_bytes = B.swa_attention_bytes(wl.q_seq, wl.q_pos, window)
+        idx_bytes, idx_flops = 0, 0
+        attn_flops = B.swa_attention_flops(wl.q_pos, window)
+    names = {0: "decode_8k_b1", 1: "mtp_verify_128k_b64", 2: "swa_decode_32k_b64", 3: "decode_1m_b4",
+             4: "prefill_chunk_16k_at_112k"}
+    config = {"workload": names[W], "batch": wl.batch, "query_tokens": n_tok,
+              "context": (f"uniform [{wl.spec.seq_len_range[0]}, {wl.spec.seq_len_range[1]}]"
+                          if wl.spec.seq_len_range else str(sorted(set(int(x) for x in wl.seq_lens)))),
+              "block_tokens": 8, "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S}
+    if window is None:
+        config["topk_blocks"] = topk
+    else:
+        config["window"] = window
+    metric = METRIC if W == 1 else f"{names[W]} query-tokens/s; achieved HBM GB/s"
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": n_tok / (ms_per_step * 1e-3),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -209,21 +256,37 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "mtp_verify_128k_b64", "batch": wl.batch, "query_tokens": n_tok,
-                   "context": "uniform [98304, 131072]", "topk_blocks": topk, "block_tokens": 8,
-                   "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S},
+        "config": config,
         "achieved_hbm_gbps": (attn_bytes + idx_bytes) / (ms_per_step * 1e-3) / 1e9,
-        "step_breakdown_ms": {"indexer_topk": idx_ms, "sparse_decode": attn_ms},
-        "algorithmic_bytes": {"indexer_topk": idx_bytes, "sparse_decode": attn_bytes},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "attention_kernel<false> (sa_sparse_decode)"},
+        "step_breakdown_ms": {"indexer_topk": idx_ms,
+                              ("swa_decode" if window else "sparse_decode"): attn_ms},
+        "algorithmic_bytes": {"indexer_topk": idx_bytes, ("swa_decode" if window else "sparse_decode"): attn_bytes},
+        "algorithmic_flops": {"indexer_topk": idx_flops, ("swa_decode" if window else "sparse_decode"): attn_flops},
     }
+    kname = "attention_kernel<%s> (%s)" % (("true", "sa_swa_decode") if window else ("false", "sa_sparse_decode"))
+    if W == 4:
+        # the prefill chunk is a dense-contraction workload on paper: report MFMA utilisation
+        tf = (attn_flops + idx_flops) / (ms_per_step * 1e-3) / 1e12
+        result["mfma_utilisation"] = tf / (PEAK_BF16_TFLOPS)
+        attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": kname}
+    elif W == 3:
+        # at 1M context the index-key scan is the dominant read
+        achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                              "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                              "kernel": "sa_indexer_topk (score_kernel + select)"}
+    else:
+        achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                              "frac": achieved / PEAK_HBM_GBPS,
+                              "traffic": counter_traffic() if W == 1 else None, "kernel": kname}
     if cold_ms is not None:
-        result["cold_cache"] = {"ms_per_step": cold_ms, "sparse_decode_ms": cold_attn_ms,
+        result["cold_cache"] = {"ms_per_step": cold_ms, "attention_ms": cold_attn_ms,
                                 "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, sel_host)
+        result["cpu_baseline"] = cpu_baseline(wl, sel_host, window)
     print(json.dumps(result), flush=True)
 
 

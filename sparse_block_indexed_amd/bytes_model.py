@@ -120,3 +120,8 @@ def sparse_attention_flops(q_pos, sel_idx: np.ndarray, num_heads: int = H) -> in
 
 def indexer_flops(q_pos) -> int:
     return int(sum((int(p) // BS) * DI * 2 for p in q_pos))
+
+
+def swa_attention_flops(q_pos, window: int, num_heads: int = H) -> int:
+    """QK^T and PV flops over each token's window."""
+    return int(sum(num_heads * (int(p) - max(0, int(p) - window + 1) + 1) * D * 2 * 2 for p in q_pos))
