@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=range(5),
                     help="0 decode 8K b1, 1 MTP verify 128K b64 (default), 2 SWA 32K b64, 3 decode 1M b4, "
                          "4 prefill chunk 16K after 112K")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="partitions per (token, group) for the attention call; 0 lets the library pick")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
     args = ap.parse_args()
@@ -167,7 +169,7 @@ def main():
     window = 512 if W == 2 else None
     n_tok = wl.n_tok
     max_blocks = (window // 8 + 2) if window else topk + 1
-    S = ops.resolve_num_splits(n_tok, max_blocks, 0)
+    S = ops.resolve_num_splits(n_tok, max_blocks, args.num_splits)
     sel = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
     ws = None if window else torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk),
                                          dtype=torch.uint8, device=dev)
@@ -185,10 +187,10 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if window is None:
-            ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=0, out=out,
+            ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=S, out=out,
                               out_lse=lse, part_o=part_o, part_lse=part_lse)
         else:
-            ops.swa_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, window, SCALE, num_splits=0, out=out,
+            ops.swa_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, window, SCALE, num_splits=S, out=out,
                            out_lse=lse, part_o=part_o, part_lse=part_lse)
         if ev is not None:
             ev[2].record(stream)

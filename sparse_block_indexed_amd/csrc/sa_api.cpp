@@ -68,6 +68,9 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   a.max_pages = pd.max_pages_per_seq;
   a.num_pages = pd.num_pages;
   a.scale_log2 = softmax_scale * kLog2e;
+  // Many query tokens per sequence (a prefill chunk) re-read the same blocks:
+  // keep them cacheable then; decode-like calls stream them.
+  a.stream_kv = n_tok <= 64 * pd.batch;
   a.part_o = S > 1 ? part_o : nullptr;
   a.part_lse = S > 1 ? part_lse : nullptr;
   a.out = S == 1 ? static_cast<uint16_t*>(out) : nullptr;
@@ -104,12 +107,13 @@ size_t sa_indexer_topk_workspace_size(int n_tok, int max_pages_per_seq, int topk
 
 int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits) {
   if (num_splits > 0) return std::min(num_splits, SA_MAX_SPLITS);
-  // Fill the GPU: aim for about 1024 workgroups (4 per CU) while giving every
-  // wave of a workgroup at least one 4-block chunk.
+  // Reach about one workgroup per CU while giving every wave of a workgroup at
+  // least four 4-block chunks: extra partitions cost partial-result traffic
+  // and a merge launch, which measured slower than fewer, longer workgroups.
   const int work = std::max(1, n_tok) * sa::kGroups;
-  const int want = (1024 + work - 1) / work;
+  const int want = (256 + work - 1) / work;
   const int chunks = (std::max(1, max_blocks_per_token) + 3) / 4;
-  const int cap = std::max(1, chunks / 4);
+  const int cap = std::max(1, chunks / 16);
   return std::max(1, std::min(std::min(want, cap), SA_MAX_SPLITS));
 }
 
@@ -153,6 +157,9 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_d
   while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < 512) chunk >>= 1;
   a.chunk_blocks = chunk;
   a.bitmap_words = a.max_hist_blocks <= sa::kBitmapMaxBlocks ? (a.max_hist_blocks + 31) / 32 : 0;
+  // Many query tokens per sequence (a prefill chunk): the score product is a
+  // dense GEMM and runs on MFMA; histories must fit the finalize-only select.
+  a.use_gemm = n_tok >= 64 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
   a.cand_count = reinterpret_cast<uint32_t*>(ws + w.count_off);

@@ -60,13 +60,16 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// K/V blocks are read once per call: non-temporal loads keep them from
-// displacing reusable lines in L2 and the MALL.
-__device__ __forceinline__ u32x4 load16_stream(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// Decode calls read each K/V block about once: non-temporal loads keep them
+// from displacing reusable lines in L2 and the MALL. Calls with many query
+// tokens per sequence (a prefill chunk) re-read blocks and use ordinary loads.
+template <bool kStream>
+__device__ __forceinline__ u32x4 load16_kv(const uint8_t* p) {
+  if constexpr (kStream) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <bool kWindow>
+template <bool kWindow, bool kStream>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   __shared__ int32_t s_unit[kMaxSlots];
   __shared__ int32_t s_beta[kMaxSlots];
@@ -75,11 +78,16 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   __shared__ float s_e[kWaves][16];
   __shared__ f32x4 s_o[kWaves - 1][12][64];
 
+  // Split-major order: the workgroups resident at one time share a partition
+  // index, i.e. one slice of every token's (ascending) block list, which keeps
+  // the live part of a large cache small enough to stay in L2/MALL when the
+  // call is split.
   const int S = a.num_splits;
   const int wg = blockIdx.x;
-  const int sp = wg % S;
-  const int g = (wg / S) % kGroups;
-  const int t = wg / (S * kGroups);
+  const int per_split = a.n_tok * kGroups;
+  const int sp = wg / per_split;
+  const int g = (wg % per_split) % kGroups;
+  const int t = (wg % per_split) / kGroups;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -164,8 +172,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     const uint8_t* pk = kbase + (size_t)unit * kUnitBytes;
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
-      kr[0][i] = load16_stream(pk + i * 128);
-      kr[1][i] = load16_stream(pk + i * 128 + 64);
+      kr[0][i] = load16_kv<kStream>(pk + i * 128);
+      kr[1][i] = load16_kv<kStream>(pk + i * 128 + 64);
     }
   };
   auto load_v = [&](int c) {
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     const int unit = slot < n ? max(s_unit[slot], 0) : 0;
     const uint8_t* pv = vbase + (size_t)unit * kUnitBytes;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) vr[i] = load16_stream(pv + i * 256);
+    for (int i = 0; i < 12; ++i) vr[i] = load16_kv<kStream>(pv + i * 256);
   };
 
   // Chunks of this wave: wave, wave + 4, ... The next chunk's K is issued
@@ -327,10 +335,14 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, bool window_mode, hipStream_t stream) {
   if (a.n_tok == 0) return hipSuccess;
   const long long grid = (long long)a.n_tok * kGroups * a.num_splits;
-  if (window_mode)
-    attention_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
-  else
-    attention_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
+  const dim3 g((unsigned)grid), b(kThreads);
+  if (window_mode) {
+    if (a.stream_kv) attention_kernel<true, true><<<g, b, 0, stream>>>(a);
+    else attention_kernel<true, false><<<g, b, 0, stream>>>(a);
+  } else {
+    if (a.stream_kv) attention_kernel<false, true><<<g, b, 0, stream>>>(a);
+    else attention_kernel<false, false><<<g, b, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

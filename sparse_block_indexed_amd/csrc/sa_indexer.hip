@@ -37,7 +37,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = 4;
 constexpr int kMaxChunkBlocks = 4096;   // the host never picks a larger score chunk
-constexpr int kFuseLimit = 16384;       // histories up to this many blocks select straight from their scores
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 // index keys are read once per call
@@ -186,10 +185,10 @@ __device__ __forceinline__ float octet_sum(float v) {
 // Score one step: 8 blocks per wave, 8 lanes per block key (lane q8 holds the
 // 16-byte chunks q8 + 8i, i = 0..3, of the key, so each load instruction reads
 // whole 128-byte lines).
-template <int NQ>
-__device__ __forceinline__ void score_step(const IndexerArgs& a, const int* tok, const int* hslot, const int* ncb,
+template <int NQ, bool kHist>
+__device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslot, const int* ncb,
                                            const u32x4* s_q, const u32x4 (&kv)[4], int beta, bool in, bool ok,
-                                           int q8, uint32_t (*s_hist)[kHistBins]) {
+                                           int q8, uint32_t (*s_hist)[kHistBins], float (&sc)[NQ]) {
   // The queries are read from LDS at every step on purpose: held in registers
   // they would take the VGPRs that keep key loads in flight. The empty asm
   // makes the offset opaque so the reads are not hoisted out of the loop.
@@ -205,21 +204,23 @@ __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* tok,
       for (int w = 0; w < 4; ++w) s = dot2(kv[i][w], q[w], s);
     }
     s = octet_sum(s);
-    const float sc = ok ? s : -INFINITY;   // an unreadable page ranks last
-    if (in && q8 == j && beta < ncb[j]) {
-      a.scores[(size_t)tok[j] * a.max_hist_blocks + beta] = sc;
-      atomicAdd(&s_hist[hslot[j]][score_key(sc) >> 21], 1u);
+    sc[j] = ok ? s : -INFINITY;   // an unreadable page ranks last
+    if constexpr (kHist) {
+      if (in && q8 == j && beta < ncb[j]) atomicAdd(&s_hist[hslot[j]][score_key(sc[j]) >> 21], 1u);
     }
   }
 }
 
 // One pass over blocks [lo, hi) of one sequence for NQ of its query tokens.
-// The physical page of every block comes from s_pages (preloaded). Four steps
-// (16 KB per wave) are in flight: after a step is scored its buffer is refilled
-// with the step four ahead. Refills are unconditional (a step past hi reads the
-// cache's first key and stores nothing), so each wait leaves the other three
-// buffers' loads in flight.
-template <int NQ>
+// Each wave owns a contiguous range of blocks, walked in steps of 8 blocks
+// (one 8-lane octet per block) and groups of 4 steps. Four steps (16 KB per
+// wave) are in flight: after a step is scored its buffer is refilled with the
+// same step of the next group. Refills are unconditional (a step past the end
+// reads the cache's first key and stores nothing), so each wait leaves the
+// other buffers' loads in flight. After a group, lane (octet b, q8 < 4) holds
+// the scores of block 8*q8 + b of the group, so one store per token writes 32
+// consecutive scores (a whole 128-byte line).
+template <int NQ, bool kHist>
 __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot, const int* ncb, int lo, int hi,
                           const int32_t* s_pages, const u32x4* s_q, uint32_t (*s_hist)[kHistBins]) {
   const int lane = threadIdx.x & 63;
@@ -227,51 +228,65 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
   const int q8 = lane & 7;
   const int sub = lane >> 3;
   const int page0 = lo >> 3;
+  const int per_wave = ((hi - lo + 127) / 128) * 32;   // whole groups of 32 blocks
+  const int wlo = lo + wave * per_wave;
+  const int whi = min(hi, wlo + per_wave);
+  if (wlo >= whi) return;
+  const int ngroups = (whi - wlo + 31) / 32;
   auto locate = [&](int beta, bool& in, bool& ok) -> const uint8_t* {
-    in = beta < hi;
+    in = beta < whi;
     const int page = in ? s_pages[(beta >> 3) - page0] : -1;
     ok = in && page >= 0 && page < a.num_pages;
     const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * kKeyBytes : 0;
     return a.k_idx_cache + off + q8 * 16;
   };
-  // steps of this wave: 8 blocks each, starting at lo + 8 * wave, stride 32
-  const int first = lo + wave * 8;
-  const int nsteps = first < hi ? (hi - first + 31) / 32 : 0;
-  if (nsteps == 0) return;
   u32x4 k0[4], k1[4], k2[4], k3[4];
   bool in0, ok0, in1, ok1, in2, ok2, in3, ok3;
-  int b0 = first + sub, b1 = b0 + 32, b2 = b0 + 64, b3 = b0 + 96;
   auto fill = [&](u32x4 (&kv)[4], int beta, bool& in, bool& ok) {
     const uint8_t* p = locate(beta, in, ok);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kv[i] = load16_stream(p + i * 128);
   };
-  fill(k0, b0, in0, ok0);
-  fill(k1, b1, in1, ok1);
-  fill(k2, b2, in2, ok2);
-  fill(k3, b3, in3, ok3);
-  for (int st = 0; st < nsteps; st += 4) {
-    score_step<NQ>(a, tok, hslot, ncb, s_q, k0, b0, in0, ok0, q8, s_hist);
-    b0 += 128;
-    fill(k0, b0, in0, ok0);
-    score_step<NQ>(a, tok, hslot, ncb, s_q, k1, b1, in1, ok1, q8, s_hist);
-    b1 += 128;
-    fill(k1, b1, in1, ok1);
-    score_step<NQ>(a, tok, hslot, ncb, s_q, k2, b2, in2, ok2, q8, s_hist);
-    b2 += 128;
-    fill(k2, b2, in2, ok2);
-    score_step<NQ>(a, tok, hslot, ncb, s_q, k3, b3, in3, ok3, q8, s_hist);
-    b3 += 128;
-    fill(k3, b3, in3, ok3);
+  int base = wlo;   // first block of the current group
+  fill(k0, base + sub, in0, ok0);
+  fill(k1, base + 8 + sub, in1, ok1);
+  fill(k2, base + 16 + sub, in2, ok2);
+  fill(k3, base + 24 + sub, in3, ok3);
+  for (int g = 0; g < ngroups; ++g, base += 32) {
+    float keep[NQ], sc[NQ];
+    score_step<NQ, kHist>(a, hslot, ncb, s_q, k0, base + sub, in0, ok0, q8, s_hist, sc);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) keep[j] = sc[j];
+    fill(k0, base + 32 + sub, in0, ok0);
+    score_step<NQ, kHist>(a, hslot, ncb, s_q, k1, base + 8 + sub, in1, ok1, q8, s_hist, sc);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) keep[j] = q8 == 1 ? sc[j] : keep[j];
+    fill(k1, base + 40 + sub, in1, ok1);
+    score_step<NQ, kHist>(a, hslot, ncb, s_q, k2, base + 16 + sub, in2, ok2, q8, s_hist, sc);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) keep[j] = q8 == 2 ? sc[j] : keep[j];
+    fill(k2, base + 48 + sub, in2, ok2);
+    score_step<NQ, kHist>(a, hslot, ncb, s_q, k3, base + 24 + sub, in3, ok3, q8, s_hist, sc);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) keep[j] = q8 == 3 ? sc[j] : keep[j];
+    fill(k3, base + 56 + sub, in3, ok3);
+    const int beta = base + 8 * q8 + sub;   // the block whose scores this lane keeps (q8 < 4)
+    if (q8 < 4 && beta < whi) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j)
+        if (beta < ncb[j]) a.scores[(size_t)tok[j] * a.max_hist_blocks + beta] = keep[j];
+    }
   }
 }
 
 // Runs of up to GS query tokens of one sequence share a pass over its keys; GS
 // is the host's group size, so a one-token decode does not pay for four query
 // register sets.
-template <int GS>
+// With kHist the kernel also builds each token's 2048-bin histogram of score
+// keys (needed when the history is too long for finalize to hold all scores).
+template <int GS, bool kHist>
 __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
-  __shared__ uint32_t s_hist[GS][kHistBins];
+  __shared__ uint32_t s_hist[kHist ? GS : 1][kHistBins];
   __shared__ int32_t s_pages[kMaxChunkBlocks / kBlocksPerPage + 1];
   __shared__ u32x4 s_q[GS * (kKeyBytes / 16)];   // index queries of the current run
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
@@ -290,8 +305,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
   for (int j = 0; j < ng; ++j) any |= ncb[j] > lo;
   if (!any) return;
 
-  for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) (&s_hist[0][0])[i] = 0u;
-  __syncthreads();
+  if constexpr (kHist) {
+    for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) (&s_hist[0][0])[i] = 0u;
+    __syncthreads();
+  }
 
   uint32_t done = 0;
   for (int j0 = 0; j0 < ng; ++j0) {
@@ -319,15 +336,150 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
     for (int i = threadIdx.x; i < nq * (kKeyBytes / 16); i += kThreads)
       s_q[i] = load16(a.q_idx + (size_t)tok[i / (kKeyBytes / 16)] * kKeyBytes + (i % (kKeyBytes / 16)) * 16);
     __syncthreads();
-    if (nq == 1) score_run<1>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist);
-    if constexpr (GS >= 2) { if (nq == 2) score_run<2>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
-    if constexpr (GS >= 3) { if (nq == 3) score_run<3>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
-    if constexpr (GS >= 4) { if (nq == 4) score_run<4>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if (nq == 1) score_run<1, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist);
+    if constexpr (GS >= 2) { if (nq == 2) score_run<2, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if constexpr (GS >= 3) { if (nq == 3) score_run<3, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if constexpr (GS >= 4) { if (nq == 4) score_run<4, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+  }
+  if constexpr (kHist) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) {
+      const uint32_t v = (&s_hist[0][0])[i];
+      if (v) atomicAdd(&a.hist[(size_t)(t0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2b. score as an MFMA GEMM (calls with long runs of query tokens of one
+//     sequence, e.g. a prefill chunk, and histories of at most kFuseLimit)
+// ---------------------------------------------------------------------------
+// A workgroup owns 64 consecutive query tokens and a range of block tiles of
+// their sequence's history. Wave w computes tokens 16w..16w+15 against each
+// 32-block key tile with v_mfma_f32_16x16x32_bf16 (A = index queries, held in
+// registers; B = keys, staged through LDS rows padded to 528 bytes so that the
+// 16-byte fragment reads of 16 lanes hit 64 distinct banks). The next tile's
+// keys are loaded into registers while the current tile is multiplied. Rows of
+// another sequence than the one being processed are handled in further passes.
+constexpr int kGemmTokens = 64;
+constexpr int kGemmBlocks = 32;
+constexpr int kKeyStride = kKeyBytes + 16;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int tiles_per_wg) {
+  __shared__ uint8_t s_keys[2][kGemmBlocks * kKeyStride];
+  __shared__ int s_tok_cb[kGemmTokens];
+  __shared__ int s_tok_seq[kGemmTokens];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 15, lg = lane >> 4;
+  const int t0 = blockIdx.x * kGemmTokens;
+  const int tile0 = blockIdx.y * tiles_per_wg;
+  if (tid < kGemmTokens) {
+    int b = -1;
+    int cbt = 0;
+    if (t0 + tid < a.n_tok) cbt = min(hist_blocks(a, t0 + tid, &b), a.max_hist_blocks);
+    s_tok_cb[tid] = cbt;
+    s_tok_seq[tid] = cbt > 0 ? b : -1;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) {
-    const uint32_t v = (&s_hist[0][0])[i];
-    if (v) atomicAdd(&a.hist[(size_t)(t0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
+  // A fragments: token row 16*wave + lq, dims 32*i + 8*lg .. +8
+  const int my_row = wave * 16 + lq;
+  const int t_a = min(t0 + my_row, a.n_tok - 1);
+  u32x4 qa[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qa[i] = load16(a.q_idx + (size_t)t_a * kKeyBytes + (32 * i + 8 * lg) * 2);
+
+  uint64_t done = 0;   // rows already processed (identical in every thread)
+  for (;;) {
+    int seq = -1, hi = 0;
+    for (int r = 0; r < kGemmTokens; ++r) {
+      if ((done >> r) & 1ull) continue;
+      if (s_tok_seq[r] < 0) {
+        done |= 1ull << r;
+        continue;
+      }
+      if (seq < 0) seq = s_tok_seq[r];
+      if (s_tok_seq[r] == seq) hi = max(hi, s_tok_cb[r]);
+    }
+    if (seq < 0) break;
+    uint64_t active = 0;
+    for (int r = 0; r < kGemmTokens; ++r)
+      if (((done >> r) & 1ull) == 0 && s_tok_seq[r] == seq) active |= 1ull << r;
+    done |= active;
+    const int32_t* prow = a.page_table + (size_t)seq * a.max_pages;
+    const int ntiles = (hi + kGemmBlocks - 1) / kGemmBlocks;
+    const int tl0 = tile0, tl1 = min(ntiles, tile0 + tiles_per_wg);
+    if (tl0 >= tl1) continue;
+    // key tile staging: thread tid moves 16-byte pieces tid + 256*j (j < 4)
+    constexpr int kPieces = kGemmBlocks * (kKeyBytes / 16) / kThreads;
+    u32x4 kreg[kPieces];
+    auto fetch = [&](int tile) {
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) {
+        const int piece = tid + kThreads * j;
+        const int blk = piece >> 5, part = piece & 31;
+        const int beta = tile * kGemmBlocks + blk;
+        int page = beta < hi ? prow[beta >> 3] : -1;
+        const bool ok = page >= 0 && page < a.num_pages;
+        const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * kKeyBytes + part * 16 : 0;
+        kreg[j] = load16_stream(a.k_idx_cache + off);
+      }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) {
+        const int piece = tid + kThreads * j;
+        *reinterpret_cast<u32x4*>(&s_keys[buf][(piece >> 5) * kKeyStride + (piece & 31) * 16]) = kreg[j];
+      }
+    };
+    fetch(tl0);
+    stash(0);
+    __syncthreads();
+    for (int tile = tl0; tile < tl1; ++tile) {
+      const int buf = (tile - tl0) & 1;
+      if (tile + 1 < tl1) fetch(tile + 1);
+      constexpr int kSub = kGemmBlocks / 16;
+      f32x4 c[kSub];
+#pragma unroll
+      for (int n = 0; n < kSub; ++n) {
+        c[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u32x4 kb = *reinterpret_cast<const u32x4*>(
+              &s_keys[buf][(16 * n + lq) * kKeyStride + (32 * i + 8 * lg) * 2]);
+          c[n] = mfma_bf16(qa[i], kb, c[n]);
+        }
+      }
+      // c[n][r]: token row 16*wave + 4*lg + r, block tile*kGemmBlocks + 16*n + lq
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wave * 16 + 4 * lg + r;
+        if (((active >> row) & 1ull) == 0) continue;
+        const int t = t0 + row;
+        const int cbt = s_tok_cb[row];
+        float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+#pragma unroll
+        for (int n = 0; n < kSub; ++n) {
+          const int beta = tile * kGemmBlocks + 16 * n + lq;
+          if (beta < cbt) {
+            const int page = prow[beta >> 3];
+            srow[beta] = (page >= 0 && page < a.num_pages) ? c[n][r] : -INFINITY;
+          }
+        }
+      }
+      if (tile + 1 < tl1) {
+        __syncthreads();   // everyone is done reading the other buffer
+        stash(buf ^ 1);
+        __syncthreads();
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -407,7 +559,14 @@ struct FinalizeLds {
 __device__ uint32_t radix_kth_global(const IndexerArgs& a, FinalizeLds& s, int t, int ncand, uint32_t k,
                                      uint32_t* count_gt) {
   const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
-  for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
+  __syncthreads();
+  if (ncand <= kFuseLimit) {   // no histogram from the score pass: build the first level here
+    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < ncand; i += kFinalThreads) atomicAdd(&s.h[score_key(srow[i]) >> 21], 1u);
+  } else {
+    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
+  }
   __syncthreads();
   select_bin<kFinalThreads>(s.h, kHistBins, k, s.tmp, s.res);
   uint32_t prefix = s.res[0] << 21;
@@ -485,7 +644,21 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   const int nw = (ncand + 31) >> 5;                 // bitmap words this token needs
   uint32_t* sel_bm = s_bm;
   uint32_t* eq_bm = s_bm + a.bitmap_words;
-  for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
+  const bool fused = ncand <= kFuseLimit;
+  // a short history's scores are held in registers from here on
+  constexpr int kPer = kFuseLimit / kFinalThreads;
+  uint32_t kv[kPer];
+  if (fused) {
+    const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int beta = j * kFinalThreads + (int)threadIdx.x;
+      kv[j] = beta < ncand ? score_key(srow[beta]) : 0u;
+    }
+    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
+  } else {
+    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
+  }
   if (nw <= a.bitmap_words) {
     for (int i = threadIdx.x; i < nw; i += kFinalThreads) {
       sel_bm[i] = 0u;
@@ -494,11 +667,18 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   }
   if (threadIdx.x == 0) s.n_tz = 0;
   __syncthreads();
+  if (fused) {   // the score pass built no histogram for short histories
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int beta = j * kFinalThreads + (int)threadIdx.x;
+      if (beta < ncand) atomicAdd(&s.h[kv[j] >> 21], 1u);
+    }
+    __syncthreads();
+  }
   select_bin<kFinalThreads>(s.h, kHistBins, (uint32_t)k, s.tmp, s.res);
   const uint32_t b1 = s.res[0];
   const uint32_t above = min(s.res[1], (uint32_t)k - 1u);
   const uint32_t in_bin = s.h[b1];
-  const bool fused = ncand <= kFuseLimit;
   const uint32_t n_listed = fused ? 0u : a.cand_count[t];
   if (nw > a.bitmap_words || in_bin > (uint32_t)kTieCap || (!fused && n_listed > (uint32_t)kCandCap)) {
     select_ordered_global(a, s, t, ncand, out);
@@ -517,18 +697,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
     }
   };
   if (fused) {
-    const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
-    constexpr int kPer = kFuseLimit / kFinalThreads;
-    float sv[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int beta = j * kFinalThreads + (int)threadIdx.x;
-      sv[j] = beta < ncand ? srow[beta] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int beta = j * kFinalThreads + (int)threadIdx.x;
-      if (beta < ncand) classify(score_key(sv[j]), (uint32_t)beta);
+      if (beta < ncand) classify(kv[j], (uint32_t)beta);
     }
   } else {
     for (uint32_t i = threadIdx.x; i < n_listed; i += kFinalThreads) {
@@ -628,20 +800,39 @@ IndexerWorkspace indexer_workspace_layout(int n_tok, int max_pages_per_seq) {
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
   if (a.n_tok == 0) return hipSuccess;
-  // histograms and candidate counters sit next to each other in the workspace
-  const size_t nzero = (reinterpret_cast<const uint8_t*>(a.scores) - reinterpret_cast<const uint8_t*>(a.hist)) / 4;
-  const unsigned zblocks = (unsigned)std::min<size_t>((nzero + 1023) / 1024, 2048);
-  zero_kernel<<<zblocks, 1024, 0, stream>>>(a.hist, nzero);
+  // Histories longer than kFuseLimit need the score pass's histograms and the
+  // collect pass; shorter ones are selected by finalize alone.
+  const bool long_hist = a.max_hist_blocks > kFuseLimit;
+  if (long_hist) {   // histograms and candidate counters sit next to each other in the workspace
+    const size_t nzero = (reinterpret_cast<const uint8_t*>(a.scores) - reinterpret_cast<const uint8_t*>(a.hist)) / 4;
+    const unsigned zblocks = (unsigned)std::min<size_t>((nzero + 1023) / 1024, 2048);
+    zero_kernel<<<zblocks, 1024, 0, stream>>>(a.hist, nzero);
+  }
+  if (a.use_gemm) {
+    const int ntt = (a.n_tok + kGemmTokens - 1) / kGemmTokens;
+    const int ntiles = (a.max_hist_blocks + kGemmBlocks - 1) / kGemmBlocks;
+    // about two workgroups per CU: split the block tiles when there are few token tiles
+    int splits = 1;
+    while (splits < ntiles && (long long)ntt * splits < 512) splits <<= 1;
+    const int per = (ntiles + splits - 1) / splits;
+    score_gemm_kernel<<<dim3((unsigned)ntt, (unsigned)splits), dim3(kThreads), 0, stream>>>(a, per);
+    finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
+    return hipGetLastError();
+  }
   const int ngroups = (a.n_tok + a.group_size - 1) / a.group_size;
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const dim3 sgrid((unsigned)((long long)ngroups * nchunk));
+#define SA_SCORE(GS) \
+  (long_hist ? score_kernel<GS, true><<<sgrid, dim3(kThreads), 0, stream>>>(a) \
+             : score_kernel<GS, false><<<sgrid, dim3(kThreads), 0, stream>>>(a))
   switch (a.group_size) {
-    case 1: score_kernel<1><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
-    case 2: score_kernel<2><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
-    case 3: score_kernel<3><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
-    default: score_kernel<4><<<sgrid, dim3(kThreads), 0, stream>>>(a); break;
+    case 1: SA_SCORE(1); break;
+    case 2: SA_SCORE(2); break;
+    case 3: SA_SCORE(3); break;
+    default: SA_SCORE(4); break;
   }
-  if (a.max_hist_blocks > kFuseLimit) {
+#undef SA_SCORE
+  if (long_hist) {
     const int nck = (a.max_hist_blocks + kCollectChunk - 1) / kCollectChunk;
     collect_kernel<<<dim3((unsigned)((long long)a.n_tok * nck)), dim3(kThreads), 0, stream>>>(a);
   }

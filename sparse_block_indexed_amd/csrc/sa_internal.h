@@ -24,6 +24,7 @@ constexpr int kKeyBytes = kIdxDim * 2;                     // one index key
 constexpr int kHistBins = 2048;       // first radix digit: key bits 31..21
 constexpr int kCandCap = 4096;        // candidates kept per token for the in-LDS finish
 constexpr int kCollectChunk = 4096;   // scores per collect workgroup
+constexpr int kFuseLimit = 16384;          // histories up to this many blocks are selected by finalize alone
 constexpr int kBitmapMaxBlocks = 1 << 17;   // longest history the finalize bitmaps cover (2 x 16 KB LDS)
 
 struct AttnArgs {
@@ -43,6 +44,7 @@ struct AttnArgs {
   int max_pages;
   int num_pages;
   float scale_log2;         // softmax_scale * log2(e)
+  bool stream_kv;           // non-temporal K/V loads (blocks read about once per call)
   float* part_o;            // used when num_splits > 1
   float* part_lse;
   uint16_t* out;            // used when num_splits == 1
@@ -65,6 +67,7 @@ struct IndexerArgs {
   int group_size;           // query tokens scored per pass over a sequence's keys
   int chunk_blocks;         // blocks per score workgroup
   int bitmap_words;         // LDS bitmap words per finalize workgroup (0: ordered select over all scores)
+  bool use_gemm;            // score with the MFMA GEMM kernel (long runs of tokens per sequence)
   int32_t* sel_idx;
   uint32_t* hist;           // [n_tok][kHistBins]
   uint32_t* cand_count;     // [n_tok]

@@ -59,9 +59,9 @@ def test_workspace_size(lib):
 def test_resolve_num_splits(lib):
     r = lib.sa_resolve_num_splits
     assert r(256, 513, 0) == 1          # 128K verify batch: the grid already fills the GPU
-    assert r(1, 513, 0) == 32           # one token: spread its 129 chunks over 32 partitions
-    assert r(64, 66, 0) == 4            # sliding window, batch 64
-    assert r(4, 513, 0) == 32
+    assert r(1, 513, 0) == 8            # one token: 129 chunks over 8 partitions (4 chunks per wave)
+    assert r(64, 66, 0) == 1            # sliding window, batch 64: one workgroup per (token, group)
+    assert r(4, 513, 0) == 8
     assert r(1, 1, 0) == 1              # nothing to split
     assert r(3, 513, 7) == 7            # explicit value kept
     assert r(3, 513, 1000) == 64        # clamped

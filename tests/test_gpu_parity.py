@@ -303,3 +303,15 @@ def test_zero_tokens_is_a_no_op():
     out, lse = ops.sparse_decode(wl.q[:0], wl.k_cache, wl.v_cache, pt, sl, e, e, sel, SCALE)
     torch.cuda.synchronize()
     assert sel.shape == (0, 512) and out.shape == (0, 64, 192)
+
+
+def test_prefill_gemm_path_mixed_tiles():
+    """Enough tokens per sequence for the MFMA score GEMM; the second 64-token
+    tile holds tokens of both sequences and one invalid token."""
+    _say("gemm mixed tiles")
+    spec = I.WorkloadSpec("gemm_mixed", batch=2, seq_lens=[5000, 20000], q_per_seq=70)
+    wl = I.make_workload(spec, seed=41, device="cuda")
+    wl.q_pos[100] = int(wl.seq_lens[1])      # out of range: attends nothing
+    sel, out, lse = run_sparse_layer(wl)
+    assert (sel[100] == -1).all() and (out[100] == 0).all()
+    _check_all(wl, sel, out, lse, [t for t in range(wl.n_tok) if t != 100], what="gemm mixed")
