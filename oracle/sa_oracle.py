@@ -23,6 +23,9 @@ Readings where the pages are silent (each is listed in the design notes):
 * Index score = plain dot product of the token's 256-dim index query with the
   block key; no scale, no activation (any positive scale leaves the ranking
   unchanged).
+* Index keys may also be stored in one byte (OCP FP8 E4M3), the open-weights
+  blog's "one or two bytes" per key value ("What sparse attention does and
+  doesn't save"); the score is the same dot product of the decoded values.
 * One selection per query token, shared by all four KV groups.
 * Historical blocks of a token at position p are blocks 0 .. floor(p/8)-1; the
   current block floor(p/8) is always attended, its tokens up to p only.
@@ -55,6 +58,20 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) to float64; exact, since bf16 is the top half of fp32."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) to float64, from the format's definition:
+    sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 holds
+    subnormals m * 2^-9; the all-ones exponent with all-ones mantissa is NaN
+    (the format has no infinities)."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = sign * val
+    return np.where((e == 15) & (m == 7), np.nan, val)
 
 
 # ---------------------------------------------------------------------------
@@ -95,12 +112,16 @@ def v_rows(v_cache_bits: np.ndarray, page_row: np.ndarray, positions, g: int) ->
     return out
 
 
-def index_keys(kidx_bits: np.ndarray, page_row: np.ndarray, n_blocks: int) -> np.ndarray:
-    """Index keys (float64 [n_blocks][256]) of blocks 0 .. n_blocks-1 of one sequence."""
+def index_keys(kidx_bits: np.ndarray, page_row: np.ndarray, n_blocks: int, fp8: bool = False) -> np.ndarray:
+    """Index keys (float64 [n_blocks][256]) of blocks 0 .. n_blocks-1 of one sequence.
+
+    The cache holds bf16 bit patterns (uint16), or with fp8=True one-byte OCP
+    E4M3 codes (uint8), as [page][8 blocks][256]."""
     arr = np.asarray(kidx_bits).reshape(-1, BPP, DI)
+    decode = fp8_e4m3_to_f64 if fp8 else bf16_to_f64
     out = np.empty((n_blocks, arr.shape[2]), dtype=np.float64)
     for beta in range(n_blocks):
-        out[beta] = bf16_to_f64(arr[int(page_row[beta // BPP]), beta % BPP])
+        out[beta] = decode(arr[int(page_row[beta // BPP]), beta % BPP])
     return out
 
 

@@ -335,3 +335,43 @@ def test_merge_of_split_equals_unsplit(splits):
 def test_merge_all_empty():
     mo, ml = O.merge(np.zeros((2, 64, 192)), np.full((2, 64), -np.inf))
     assert (mo == 0).all() and np.isneginf(ml).all()
+
+
+# ---------------------------------------------------------------------------
+# One-byte index keys: OCP FP8 E4M3 decoding
+# ---------------------------------------------------------------------------
+
+def test_fp8_e4m3_hand_values():
+    codes = np.array([0x00, 0x80, 0x38, 0xB8, 0x40, 0x44, 0x48, 0x7E, 0xFE, 0x01, 0x08, 0x07, 0x7F, 0xFF],
+                     dtype=np.uint8)
+    v = O.fp8_e4m3_to_f64(codes)
+    assert v[0] == 0.0 and not np.signbit(v[0])
+    assert v[1] == 0.0 and np.signbit(v[1])
+    assert v[2] == 1.0 and v[3] == -1.0
+    assert v[4] == 2.0 and v[5] == 3.0 and v[6] == 4.0
+    assert v[7] == 448.0 and v[8] == -448.0          # largest finite
+    assert v[9] == 2.0 ** -9                          # smallest subnormal
+    assert v[10] == 2.0 ** -6                         # smallest normal
+    assert v[11] == 7 * 2.0 ** -9                     # largest subnormal
+    assert np.isnan(v[12]) and np.isnan(v[13])
+
+
+def test_fp8_e4m3_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.fp8_e4m3_to_f64(codes)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert ((ref == got) | both_nan).all()
+    assert (np.signbit(ref) == np.signbit(got))[~both_nan].all()
+
+
+def test_fp8_keys_give_the_bf16_selection_for_small_integers():
+    rng = np.random.default_rng(8)
+    ints = rng.integers(-4, 5, size=(3, 8, 256))
+    bf = torch.from_numpy(ints).to(torch.bfloat16)
+    f8 = torch.from_numpy(ints).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    page_row = np.array([2, 0, 1])
+    k_bf = O.index_keys(I.bf16_bits(bf), page_row, 20)
+    k_f8 = O.index_keys(f8, page_row, 20, fp8=True)
+    np.testing.assert_array_equal(k_bf, k_f8)
+    np.testing.assert_array_equal(k_f8[9], ints[0, 1])      # block 9 = logical page 1 -> physical 0, block 1
