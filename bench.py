@@ -135,6 +135,8 @@ def main():
                          "4 prefill chunk 16K after 112K")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="partitions per (token, group) for the attention call; 0 lets the library pick")
+    ap.add_argument("--fp8-index-keys", action="store_true",
+                    help="score one-byte (OCP E4M3) index keys: the same integer values, half the bytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
     args = ap.parse_args()
@@ -165,6 +167,7 @@ def main():
     W = args.workload
     wl = I.config_workload(W, device=dev)
     pt, sl, qs, qp = wl.device_ints(dev)
+    kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if args.fp8_index_keys else wl.k_idx_cache
     topk = 512
     window = 512 if W == 2 else None
     n_tok = wl.n_tok
@@ -183,7 +186,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         if window is None:
-            ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
+            ops.indexer_topk(wl.q_idx, kidx, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
         if window is None:
@@ -227,7 +230,7 @@ def main():
     sel_host = sel.cpu().numpy() if window is None else None
     if window is None:
         attn_bytes = B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host)
-        idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk)
+        idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk, key_bytes=1 if args.fp8_index_keys else 2)
         attn_flops = B.sparse_attention_flops(wl.q_pos, sel_host)
         idx_flops = B.indexer_flops(wl.q_pos)
     else:
@@ -242,9 +245,11 @@ def main():
               "block_tokens": 8, "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S}
     if window is None:
         config["topk_blocks"] = topk
+        config["index_keys"] = "fp8_e4m3" if args.fp8_index_keys else "bf16"
     else:
         config["window"] = window
-    metric = METRIC if W == 1 else f"{names[W]} query-tokens/s; achieved HBM GB/s"
+    metric = METRIC if (W == 1 and not args.fp8_index_keys) else \
+        f"{names[W]}{' (fp8 index keys)' if args.fp8_index_keys else ''} query-tokens/s; achieved HBM GB/s"
     result = {
         "metric": metric,
         "value": n_tok / (ms_per_step * 1e-3),

@@ -112,6 +112,23 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_d
                           const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
                           int32_t* sel_idx, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The same selection with one-byte index keys. (Open-weights blog, "What
+ * sparse attention does and doesn't save": index keys at one or two bytes per
+ * value; one byte halves the scan that dominates at long context.)
+ *
+ * k_idx_cache_fp8  device uint8 [num_pages][8][256], OCP FP8 E4M3 codes (sign,
+ *                  4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ *                  S.1111.111 is NaN). Keys are widened exactly to bf16 and
+ *                  scored like sa_indexer_topk; q_idx stays bf16. Every other
+ *                  argument, the workspace size and the result are as for
+ *                  sa_indexer_topk. Integers -4..4 are exact in E4M3, so such
+ *                  keys give the same selection as their bf16 form.
+ */
+sa_status sa_indexer_topk_fp8(const void* q_idx, const void* k_idx_cache_fp8, sa_paged_desc pd,
+                              const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
+                              int32_t* sel_idx, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Number of partitions a decode call uses for a given request
  * (num_splits > 0 is returned clamped to SA_MAX_SPLITS; 0 picks from n_tok and
  * max_blocks_per_token so that the grid fills the GPU). */

@@ -49,14 +49,14 @@ def indexer_read_bytes_per_step(context: int, sparse_layers: int = 23, key_bytes
 # Per-launch algorithmic traffic of this library's kernels
 # ---------------------------------------------------------------------------
 
-def indexer_topk_bytes(q_seq: np.ndarray, q_pos: np.ndarray, topk: int) -> int:
-    """Each sequence's index keys once (up to its longest history), the index
-    queries, and the selection written."""
+def indexer_topk_bytes(q_seq: np.ndarray, q_pos: np.ndarray, topk: int, key_bytes: int = BF16) -> int:
+    """Each sequence's index keys once (up to its longest history; key_bytes per
+    value), the index queries, and the selection written."""
     q_seq = np.asarray(q_seq)
     q_pos = np.asarray(q_pos)
     total = 0
     for b in np.unique(q_seq):
-        total += int((q_pos[q_seq == b] // BS).max()) * DI * BF16
+        total += int((q_pos[q_seq == b] // BS).max()) * DI * key_bytes
     total += len(q_seq) * DI * BF16          # index queries
     total += len(q_seq) * topk * 4           # sel_idx (int32)
     return total

@@ -117,9 +117,9 @@ int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits) {
   return std::max(1, std::min(std::min(want, cap), SA_MAX_SPLITS));
 }
 
-sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_desc pd, const int32_t* q_seq,
-                          const int32_t* q_pos, int n_tok, int topk, int32_t* sel_idx, void* workspace,
-                          size_t ws_bytes, hipStream_t stream) {
+static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, bool key_fp8, sa_paged_desc pd,
+                                   const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
+                                   int32_t* sel_idx, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (n_tok < 0) return SA_ERR_INVALID_ARG;
   if (n_tok == 0) return SA_OK;
   if (q_idx == nullptr || k_idx_cache == nullptr || sel_idx == nullptr || workspace == nullptr)
@@ -160,6 +160,7 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_d
   // Many query tokens per sequence (a prefill chunk): the score product is a
   // dense GEMM and runs on MFMA; histories must fit the finalize-only select.
   a.use_gemm = n_tok >= 64 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
+  a.key_fp8 = key_fp8;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
   a.cand_count = reinterpret_cast<uint32_t*>(ws + w.count_off);
@@ -168,6 +169,20 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_d
   a.sel_idx = sel_idx;
   if (sa::launch_indexer_topk(a, stream) != hipSuccess) return SA_ERR_HIP;
   return SA_OK;
+}
+
+sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_desc pd, const int32_t* q_seq,
+                          const int32_t* q_pos, int n_tok, int topk, int32_t* sel_idx, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  return indexer_topk_impl(q_idx, k_idx_cache, false, pd, q_seq, q_pos, n_tok, topk, sel_idx, workspace, ws_bytes,
+                           stream);
+}
+
+sa_status sa_indexer_topk_fp8(const void* q_idx, const void* k_idx_cache_fp8, sa_paged_desc pd,
+                              const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk, int32_t* sel_idx,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return indexer_topk_impl(q_idx, k_idx_cache_fp8, true, pd, q_seq, q_pos, n_tok, topk, sel_idx, workspace,
+                           ws_bytes, stream);
 }
 
 sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,

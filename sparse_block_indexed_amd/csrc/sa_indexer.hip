@@ -12,7 +12,8 @@
 //  1. zero      clear the per-token histograms and candidate counters.
 //  2. score     stream every historical index key of a sequence once and score
 //               all of that sequence's query tokens against it (v_dot2 bf16 ->
-//               fp32, eight lanes per key, DPP reduction); write fp32 scores
+//               fp32, eight lanes per key, DPP reduction; one-byte E4M3 keys
+//               are widened to bf16 first); write fp32 scores
 //               and add each score to a 2048-bin histogram of the top 11 bits
 //               of its order-preserving key.
 //  3. collect   per (token, score chunk): find the histogram bin that holds the
@@ -185,10 +186,26 @@ __device__ __forceinline__ float octet_sum(float v) {
 // Score one step: 8 blocks per wave, 8 lanes per block key (lane q8 holds the
 // 16-byte chunks q8 + 8i, i = 0..3, of the key, so each load instruction reads
 // whole 128-byte lines).
-template <int NQ, bool kHist>
+// Key bytes per block and 16-byte loads per lane (8 lanes per key).
+template <bool kFp8> struct KeyFmt {
+  static constexpr int kBytes = kFp8 ? kKeyBytes / 2 : kKeyBytes;
+  static constexpr int kLoads = kBytes / 128;
+};
+
+// Two OCP E4M3 bytes (selected half of a 32-bit word) to a bf16 pair; exact.
+template <bool kHiHalf>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHiHalf));
+}
+
+// Score one step for NQ query tokens. Lane q8 of a block's octet holds the
+// 16-byte chunks q8 + 8i of the key: for bf16 keys 8 dims each (i < 4), for fp8
+// keys 16 dims each (i < 2), converted to bf16 pairs before the v_dot2.
+template <int NQ, bool kHist, bool kFp8>
 __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslot, const int* ncb,
-                                           const u32x4* s_q, const u32x4 (&kv)[4], int beta, bool in, bool ok,
-                                           int q8, uint32_t (*s_hist)[kHistBins], float (&sc)[NQ]) {
+                                           const u32x4* s_q, const u32x4 (&kv)[KeyFmt<kFp8>::kLoads], int beta,
+                                           bool in, bool ok, int q8, uint32_t (*s_hist)[kHistBins],
+                                           float (&sc)[NQ]) {
   // The queries are read from LDS at every step on purpose: held in registers
   // they would take the VGPRs that keep key loads in flight. The empty asm
   // makes the offset opaque so the reads are not hoisted out of the loop.
@@ -197,11 +214,27 @@ __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslo
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     float s = 0.f;
+    if constexpr (!kFp8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 q = s_q[j * (kKeyBytes / 16) + qoff + 8 * i];   // broadcast read
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 q = s_q[j * (kKeyBytes / 16) + qoff + 8 * i];   // broadcast read
 #pragma unroll
-      for (int w = 0; w < 4; ++w) s = dot2(kv[i][w], q[w], s);
+        for (int w = 0; w < 4; ++w) s = dot2(kv[i][w], q[w], s);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // key dims (q8 + 8i) * 16 .. +16 <-> query u32x4 2 * (q8 + 8i) and the next
+        const u32x4 q0 = s_q[j * (kKeyBytes / 16) + 2 * (qoff + 8 * i)];
+        const u32x4 q1 = s_q[j * (kKeyBytes / 16) + 2 * (qoff + 8 * i) + 1];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t qa = w < 2 ? q0[2 * w] : q1[2 * (w - 2)];
+          const uint32_t qb = w < 2 ? q0[2 * w + 1] : q1[2 * (w - 2) + 1];
+          s = dot2(fp8x2_to_bf16x2<false>(kv[i][w]), qa, s);
+          s = dot2(fp8x2_to_bf16x2<true>(kv[i][w]), qb, s);
+        }
+      }
     }
     s = octet_sum(s);
     sc[j] = ok ? s : -INFINITY;   // an unreadable page ranks last
@@ -220,9 +253,11 @@ __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslo
 // other buffers' loads in flight. After a group, lane (octet b, q8 < 4) holds
 // the scores of block 8*q8 + b of the group, so one store per token writes 32
 // consecutive scores (a whole 128-byte line).
-template <int NQ, bool kHist>
+template <int NQ, bool kHist, bool kFp8>
 __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot, const int* ncb, int lo, int hi,
                           const int32_t* s_pages, const u32x4* s_q, uint32_t (*s_hist)[kHistBins]) {
+  constexpr int KB = KeyFmt<kFp8>::kBytes;
+  constexpr int KL = KeyFmt<kFp8>::kLoads;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q8 = lane & 7;
@@ -237,15 +272,15 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
     in = beta < whi;
     const int page = in ? s_pages[(beta >> 3) - page0] : -1;
     ok = in && page >= 0 && page < a.num_pages;
-    const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * kKeyBytes : 0;
+    const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * KB : 0;
     return a.k_idx_cache + off + q8 * 16;
   };
-  u32x4 k0[4], k1[4], k2[4], k3[4];
+  u32x4 k0[KL], k1[KL], k2[KL], k3[KL];
   bool in0, ok0, in1, ok1, in2, ok2, in3, ok3;
-  auto fill = [&](u32x4 (&kv)[4], int beta, bool& in, bool& ok) {
+  auto fill = [&](u32x4 (&kv)[KL], int beta, bool& in, bool& ok) {
     const uint8_t* p = locate(beta, in, ok);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kv[i] = load16_stream(p + i * 128);
+    for (int i = 0; i < KL; ++i) kv[i] = load16_stream(p + i * 128);
   };
   int base = wlo;   // first block of the current group
   fill(k0, base + sub, in0, ok0);
@@ -254,19 +289,19 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
   fill(k3, base + 24 + sub, in3, ok3);
   for (int g = 0; g < ngroups; ++g, base += 32) {
     float keep[NQ], sc[NQ];
-    score_step<NQ, kHist>(a, hslot, ncb, s_q, k0, base + sub, in0, ok0, q8, s_hist, sc);
+    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k0, base + sub, in0, ok0, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = sc[j];
     fill(k0, base + 32 + sub, in0, ok0);
-    score_step<NQ, kHist>(a, hslot, ncb, s_q, k1, base + 8 + sub, in1, ok1, q8, s_hist, sc);
+    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k1, base + 8 + sub, in1, ok1, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 1 ? sc[j] : keep[j];
     fill(k1, base + 40 + sub, in1, ok1);
-    score_step<NQ, kHist>(a, hslot, ncb, s_q, k2, base + 16 + sub, in2, ok2, q8, s_hist, sc);
+    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k2, base + 16 + sub, in2, ok2, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 2 ? sc[j] : keep[j];
     fill(k2, base + 48 + sub, in2, ok2);
-    score_step<NQ, kHist>(a, hslot, ncb, s_q, k3, base + 24 + sub, in3, ok3, q8, s_hist, sc);
+    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k3, base + 24 + sub, in3, ok3, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 3 ? sc[j] : keep[j];
     fill(k3, base + 56 + sub, in3, ok3);
@@ -284,7 +319,7 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
 // register sets.
 // With kHist the kernel also builds each token's 2048-bin histogram of score
 // keys (needed when the history is too long for finalize to hold all scores).
-template <int GS, bool kHist>
+template <int GS, bool kHist, bool kFp8>
 __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
   __shared__ uint32_t s_hist[kHist ? GS : 1][kHistBins];
   __shared__ int32_t s_pages[kMaxChunkBlocks / kBlocksPerPage + 1];
@@ -336,10 +371,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
     for (int i = threadIdx.x; i < nq * (kKeyBytes / 16); i += kThreads)
       s_q[i] = load16(a.q_idx + (size_t)tok[i / (kKeyBytes / 16)] * kKeyBytes + (i % (kKeyBytes / 16)) * 16);
     __syncthreads();
-    if (nq == 1) score_run<1, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist);
-    if constexpr (GS >= 2) { if (nq == 2) score_run<2, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
-    if constexpr (GS >= 3) { if (nq == 3) score_run<3, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
-    if constexpr (GS >= 4) { if (nq == 4) score_run<4, kHist>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if (nq == 1) score_run<1, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist);
+    if constexpr (GS >= 2) { if (nq == 2) score_run<2, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if constexpr (GS >= 3) { if (nq == 3) score_run<3, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if constexpr (GS >= 4) { if (nq == 4) score_run<4, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
   }
   if constexpr (kHist) {
     __syncthreads();
@@ -373,7 +408,9 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  0, 0, 0);
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int tiles_per_wg) {
+  constexpr int KB = KeyFmt<kFp8>::kBytes;
   __shared__ uint8_t s_keys[2][kGemmBlocks * kKeyStride];
   __shared__ int s_tok_cb[kGemmTokens];
   __shared__ int s_tok_seq[kGemmTokens];
@@ -416,18 +453,20 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
     const int ntiles = (hi + kGemmBlocks - 1) / kGemmBlocks;
     const int tl0 = tile0, tl1 = min(ntiles, tile0 + tiles_per_wg);
     if (tl0 >= tl1) continue;
-    // key tile staging: thread tid moves 16-byte pieces tid + 256*j (j < 4)
-    constexpr int kPieces = kGemmBlocks * (kKeyBytes / 16) / kThreads;
+    // key tile staging: thread tid moves 16-byte pieces tid + 256*j of the
+    // tile's keys (bf16: 8 dims per piece; fp8: 16 dims, widened to bf16 in LDS)
+    constexpr int kPieces = kGemmBlocks * (KB / 16) / kThreads;
+    constexpr int kPerKey = KB / 16;
     u32x4 kreg[kPieces];
     auto fetch = [&](int tile) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
         const int piece = tid + kThreads * j;
-        const int blk = piece >> 5, part = piece & 31;
+        const int blk = piece / kPerKey, part = piece % kPerKey;
         const int beta = tile * kGemmBlocks + blk;
         int page = beta < hi ? prow[beta >> 3] : -1;
         const bool ok = page >= 0 && page < a.num_pages;
-        const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * kKeyBytes + part * 16 : 0;
+        const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * KB + part * 16 : 0;
         kreg[j] = load16_stream(a.k_idx_cache + off);
       }
     };
@@ -435,7 +474,21 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
         const int piece = tid + kThreads * j;
-        *reinterpret_cast<u32x4*>(&s_keys[buf][(piece >> 5) * kKeyStride + (piece & 31) * 16]) = kreg[j];
+        const int blk = piece / kPerKey, part = piece % kPerKey;
+        if constexpr (!kFp8) {
+          *reinterpret_cast<u32x4*>(&s_keys[buf][blk * kKeyStride + part * 16]) = kreg[j];
+        } else {
+          u32x4 lo, hi2;
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            lo[2 * w] = fp8x2_to_bf16x2<false>(kreg[j][w]);
+            lo[2 * w + 1] = fp8x2_to_bf16x2<true>(kreg[j][w]);
+            hi2[2 * w] = fp8x2_to_bf16x2<false>(kreg[j][w + 2]);
+            hi2[2 * w + 1] = fp8x2_to_bf16x2<true>(kreg[j][w + 2]);
+          }
+          *reinterpret_cast<u32x4*>(&s_keys[buf][blk * kKeyStride + part * 32]) = lo;
+          *reinterpret_cast<u32x4*>(&s_keys[buf][blk * kKeyStride + part * 32 + 16]) = hi2;
+        }
       }
     };
     fetch(tl0);
@@ -815,16 +868,26 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
     int splits = 1;
     while (splits < ntiles && (long long)ntt * splits < 512) splits <<= 1;
     const int per = (ntiles + splits - 1) / splits;
-    score_gemm_kernel<<<dim3((unsigned)ntt, (unsigned)splits), dim3(kThreads), 0, stream>>>(a, per);
+    if (a.key_fp8)
+      score_gemm_kernel<true><<<dim3((unsigned)ntt, (unsigned)splits), dim3(kThreads), 0, stream>>>(a, per);
+    else
+      score_gemm_kernel<false><<<dim3((unsigned)ntt, (unsigned)splits), dim3(kThreads), 0, stream>>>(a, per);
     finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
     return hipGetLastError();
   }
   const int ngroups = (a.n_tok + a.group_size - 1) / a.group_size;
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const dim3 sgrid((unsigned)((long long)ngroups * nchunk));
-#define SA_SCORE(GS) \
-  (long_hist ? score_kernel<GS, true><<<sgrid, dim3(kThreads), 0, stream>>>(a) \
-             : score_kernel<GS, false><<<sgrid, dim3(kThreads), 0, stream>>>(a))
+#define SA_SCORE(GS)                                                                     \
+  do {                                                                                   \
+    if (a.key_fp8) {                                                                     \
+      if (long_hist) score_kernel<GS, true, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);   \
+      else score_kernel<GS, false, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);            \
+    } else {                                                                             \
+      if (long_hist) score_kernel<GS, true, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);  \
+      else score_kernel<GS, false, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);           \
+    }                                                                                    \
+  } while (0)
   switch (a.group_size) {
     case 1: SA_SCORE(1); break;
     case 2: SA_SCORE(2); break;

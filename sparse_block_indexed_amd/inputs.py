@@ -209,6 +209,12 @@ def pack_index_key(k_idx_cache: torch.Tensor, page_table_row: np.ndarray, block:
     k_idx_cache[page, block % BPP, :] = key.to(k_idx_cache.dtype)
 
 
+def fp8_e4m3_codes(t: torch.Tensor) -> torch.Tensor:
+    """One-byte OCP E4M3 codes (uint8) of a tensor's values, rounded by torch
+    (exact for the small integers of the index inputs)."""
+    return t.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor as a numpy uint16 array (host copy)."""
     assert t.dtype == torch.bfloat16

@@ -21,7 +21,7 @@ MAX_TOPK = 512
 MAX_SPLITS = 64
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
-EXPORTED = ["sa_status_string", "sa_indexer_topk_workspace_size", "sa_indexer_topk",
+EXPORTED = ["sa_status_string", "sa_indexer_topk_workspace_size", "sa_indexer_topk", "sa_indexer_topk_fp8",
             "sa_resolve_num_splits", "sa_sparse_decode", "sa_swa_decode", "sa_merge"]
 
 
@@ -55,8 +55,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sa_indexer_topk_workspace_size.argtypes = [i32, i32, i32]
     lib.sa_resolve_num_splits.restype = i32
     lib.sa_resolve_num_splits.argtypes = [i32, i32, i32]
-    lib.sa_indexer_topk.restype = i32
-    lib.sa_indexer_topk.argtypes = [vp, vp, PagedDesc, vp, vp, i32, i32, vp, vp, sz, vp]
+    for fn in (lib.sa_indexer_topk, lib.sa_indexer_topk_fp8):
+        fn.restype = i32
+        fn.argtypes = [vp, vp, PagedDesc, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.sa_sparse_decode.restype = i32
     lib.sa_sparse_decode.argtypes = [vp, vp, vp, PagedDesc, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp]
     lib.sa_swa_decode.restype = i32
@@ -110,12 +111,18 @@ def resolve_num_splits(n_tok: int, max_blocks_per_token: int, num_splits: int = 
 
 def indexer_topk(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk: int = MAX_TOPK,
                  sel_idx=None, workspace=None, stream=None):
-    """Top-k historical blocks per query token (ascending, -1 padded): int32 [n_tok][topk]."""
+    """Top-k historical blocks per query token (ascending, -1 padded): int32 [n_tok][topk].
+
+    k_idx_cache is bf16, or one-byte OCP E4M3 keys (torch.float8_e4m3fn, or
+    their codes as torch.uint8), which go to sa_indexer_topk_fp8."""
     lib = load_library()
     dev = q_idx.device
     n_tok = q_idx.shape[0]
     _need(q_idx, "q_idx", torch.bfloat16, dev, (n_tok, DI))
-    _need(k_idx_cache, "k_idx_cache", torch.bfloat16, dev)
+    fp8 = k_idx_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8:
+        k_idx_cache = k_idx_cache.view(torch.uint8)
+    _need(k_idx_cache, "k_idx_cache", torch.uint8 if fp8 else torch.bfloat16, dev)
     if k_idx_cache.dim() != 3 or tuple(k_idx_cache.shape[1:]) != (8, DI):
         raise ValueError("k_idx_cache: expected [num_pages][8][256]")
     _need(q_seq, "q_seq", torch.int32, dev, (n_tok,))
@@ -128,9 +135,10 @@ def indexer_topk(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk: i
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev)
-    st = lib.sa_indexer_topk(_ptr(q_idx), _ptr(k_idx_cache), pd, _ptr(q_seq), _ptr(q_pos), n_tok, topk,
-                             _ptr(sel_idx), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check("sa_indexer_topk", st)
+    fn = lib.sa_indexer_topk_fp8 if fp8 else lib.sa_indexer_topk
+    st = fn(_ptr(q_idx), _ptr(k_idx_cache), pd, _ptr(q_seq), _ptr(q_pos), n_tok, topk, _ptr(sel_idx),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("sa_indexer_topk_fp8" if fp8 else "sa_indexer_topk", st)
     return sel_idx
 
 

@@ -21,10 +21,10 @@ def device_tables(wl, device="cuda"):
     return wl.device_ints(device)
 
 
-def run_sparse_layer(wl, topk=512, num_splits=0, scale=SCALE, tabs=None):
+def run_sparse_layer(wl, topk=512, num_splits=0, scale=SCALE, tabs=None, kidx=None):
     from sparse_block_indexed_amd import ops
     pt, sl, qs, qp = tabs if tabs is not None else device_tables(wl)
-    sel = ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk)
+    sel = ops.indexer_topk(wl.q_idx, wl.k_idx_cache if kidx is None else kidx, pt, sl, qs, qp, topk)
     out, lse = ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return sel, out, lse
@@ -39,10 +39,12 @@ def run_swa(wl, window=512, num_splits=0, scale=SCALE, tabs=None):
 
 
 class OracleView:
-    """Host-side oracle over a device workload; caches each sequence's index keys."""
+    """Host-side oracle over a device workload; caches each sequence's index keys.
+    With kidx_fp8 (uint8 E4M3 codes) the index keys are read from it instead."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, kidx_fp8=None):
         self.wl = wl
+        self.kidx_fp8 = kidx_fp8
         self._keys = {}
 
     def keys(self, b, cb):
@@ -50,8 +52,12 @@ class OracleView:
         if have is None or have.shape[0] < cb:
             npg = (cb + 7) // 8
             pages = torch.as_tensor(self.wl.page_table[b, :npg].astype(np.int64), device=self.wl.k_idx_cache.device)
-            kidx = I.bf16_bits(self.wl.k_idx_cache.index_select(0, pages))
-            have = O.index_keys(kidx, np.arange(npg), npg * 8)
+            if self.kidx_fp8 is None:
+                kidx = I.bf16_bits(self.wl.k_idx_cache.index_select(0, pages))
+                have = O.index_keys(kidx, np.arange(npg), npg * 8)
+            else:
+                kidx = self.kidx_fp8.index_select(0, pages).cpu().numpy()
+                have = O.index_keys(kidx, np.arange(npg), npg * 8, fp8=True)
             self._keys[b] = have
         return have[:cb]
 

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ["sa_indexer_topk", "sa_sparse_decode", "sa_swa_decode", "sa_merge",
+    for n in ["sa_indexer_topk", "sa_indexer_topk_fp8", "sa_sparse_decode", "sa_swa_decode", "sa_merge",
               "sa_indexer_topk_workspace_size", "sa_status_string", "sa_resolve_num_splits"]:
         assert n in names
 
@@ -92,6 +92,11 @@ def test_indexer_topk_validation(lib):
     assert f(P, P, _desc(ops, batch=0), P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
     assert f(P, P, _desc(ops, pt=0), P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
     assert f(P, P, _desc(ops, num_pages=1 << 26), P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+    f8 = lib.sa_indexer_topk_fp8
+    assert f8(None, None, d, None, None, 0, 512, None, None, 0, None) == ops.SA_OK
+    assert f8(P, None, d, P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
+    assert f8(P, P, d, P, P, 4, 600, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+    assert f8(P, P, d, P, P, 4, 512, P, P, ws - 1, None) == ops.SA_ERR_WORKSPACE
 
 
 def test_sparse_decode_validation(lib):

@@ -315,3 +315,54 @@ def test_prefill_gemm_path_mixed_tiles():
     sel, out, lse = run_sparse_layer(wl)
     assert (sel[100] == -1).all() and (out[100] == 0).all()
     _check_all(wl, sel, out, lse, [t for t in range(wl.n_tok) if t != 100], what="gemm mixed")
+
+
+# ---------------------------------------------------------------------------
+# One-byte (OCP FP8 E4M3) index keys
+# ---------------------------------------------------------------------------
+
+def _check_selection(wl, sel, tokens, topk=512, kidx_fp8=None, what=""):
+    ov = OracleView(wl, kidx_fp8=kidx_fp8)
+    sel_h = sel.cpu().numpy()
+    for t in tokens:
+        assert sel_h[t].tolist() == ov.selection(t, topk).tolist(), f"{what}: token {t}"
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_fp8_index_keys_match_bf16_and_oracle(cfg):
+    """Integer keys are exact in E4M3: the one-byte path must select exactly what
+    the bf16 path and the oracle (decoding the codes itself) select."""
+    _say(f"fp8 keys config {cfg}")
+    from sparse_block_indexed_amd import ops
+    wl = I.config_workload(cfg, device="cuda")
+    pt, sl, qs, qp = device_tables(wl)
+    codes = I.fp8_e4m3_codes(wl.k_idx_cache)
+    sel8 = ops.indexer_topk(wl.q_idx, codes, pt, sl, qs, qp, 512)
+    sel16 = ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, 512)
+    torch.cuda.synchronize()
+    assert torch.equal(sel8, sel16)
+    sample = range(wl.n_tok) if wl.n_tok <= 8 else range(0, wl.n_tok, 16)
+    _check_selection(wl, sel8, sample, kidx_fp8=codes, what=f"fp8 cfg{cfg}")
+
+
+def test_fp8_index_keys_general_codes():
+    """Random E4M3 codes across eight binades (values 1/8 .. 30, both signs) with
+    integer queries: scores stay exact in fp32, so the selection checks the
+    hardware's decoding of every such code against the oracle's. Covers the
+    per-token scorer (short and long histories) and the prefill GEMM."""
+    _say("fp8 general codes")
+    from sparse_block_indexed_amd import ops
+    for spec in (I.WorkloadSpec("f8a", batch=3, seq_lens=[3000, 20000, 140000], q_per_seq=2),
+                 I.WorkloadSpec("f8g", batch=2, seq_lens=[5000, 9000], q_per_seq=70)):
+        wl = I.make_workload(spec, seed=52, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(6)
+        shape = wl.k_idx_cache.shape
+        e = torch.randint(4, 12, shape, generator=g, device="cuda", dtype=torch.int32)
+        m = torch.randint(0, 8, shape, generator=g, device="cuda", dtype=torch.int32)
+        sg = torch.randint(0, 2, shape, generator=g, device="cuda", dtype=torch.int32)
+        codes = ((sg << 7) | (e << 3) | m).to(torch.uint8)
+        pt, sl, qs, qp = device_tables(wl)
+        sel = ops.indexer_topk(wl.q_idx, codes, pt, sl, qs, qp, 512)
+        torch.cuda.synchronize()
+        toks = range(wl.n_tok) if wl.n_tok <= 8 else range(0, wl.n_tok, 7)
+        _check_selection(wl, sel, toks, kidx_fp8=codes, what=spec.name)
