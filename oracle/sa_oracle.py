@@ -26,6 +26,10 @@ Readings where the pages are silent (each is listed in the design notes):
 * Index keys may also be stored in one byte (OCP FP8 E4M3), the open-weights
   blog's "one or two bytes" per key value ("What sparse attention does and
   doesn't save"); the score is the same dot product of the decoded values.
+* K/V of the sparse layers may be stored in one byte (the open-weights blog,
+  "Fitting it on a node": FP8 KV for the full-attention layers, lossy): value =
+  E4M3 code * per-cache scale; attention is the same exact softmax over the
+  decoded values.
 * One selection per query token, shared by all four KV groups.
 * Historical blocks of a token at position p are blocks 0 .. floor(p/8)-1; the
   current block floor(p/8) is always attended, its tokens up to p only.
@@ -109,6 +113,38 @@ def v_rows(v_cache_bits: np.ndarray, page_row: np.ndarray, positions, g: int) ->
         r = pos % PS
         base = _unit_offset(page, g, r // BS)
         out[i] = bf16_to_f64(flat[base + d * 8 + (r % BS)])
+    return out
+
+
+# One-byte (OCP FP8 E4M3) K/V caches: the value is code * scale, with a scale
+# per cache (per layer).  Layouts:
+#   K: [page][group][block-in-page][8 tokens][192 dims]
+#   V: [page][group][block-in-page][192 dims][8 tokens]
+FP8_UNIT = BS * D
+
+
+def k_rows_fp8(k_codes: np.ndarray, page_row: np.ndarray, positions, g: int, k_scale: float) -> np.ndarray:
+    """K rows (float64 [n][192]) of the given token positions, group g, from E4M3 codes."""
+    flat = np.asarray(k_codes).reshape(-1)
+    out = np.empty((len(positions), D), dtype=np.float64)
+    for i, pos in enumerate(positions):
+        page = int(page_row[pos // PS])
+        r = pos % PS
+        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT + (r % BS) * D
+        out[i] = fp8_e4m3_to_f64(flat[base:base + D]) * k_scale
+    return out
+
+
+def v_rows_fp8(v_codes: np.ndarray, page_row: np.ndarray, positions, g: int, v_scale: float) -> np.ndarray:
+    """V rows (float64 [n][192]) of the given token positions, group g, from E4M3 codes."""
+    flat = np.asarray(v_codes).reshape(-1)
+    out = np.empty((len(positions), D), dtype=np.float64)
+    d = np.arange(D)
+    for i, pos in enumerate(positions):
+        page = int(page_row[pos // PS])
+        r = pos % PS
+        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT
+        out[i] = fp8_e4m3_to_f64(flat[base + d * BS + (r % BS)]) * v_scale
     return out
 
 
@@ -202,9 +238,15 @@ def window_positions(p: int, window: int) -> np.ndarray:
     return np.arange(max(0, p - window + 1), p + 1, dtype=np.int64)
 
 
-def attend_positions(q_heads, k_cache_bits, v_cache_bits, page_row, positions, scale):
-    ks = [k_rows(k_cache_bits, page_row, positions, g) for g in range(G)]
-    vs = [v_rows(v_cache_bits, page_row, positions, g) for g in range(G)]
+def attend_positions(q_heads, k_cache_bits, v_cache_bits, page_row, positions, scale, fp8_scales=None):
+    """Attention of one token over the given positions of its sequence. With
+    fp8_scales = (k_scale, v_scale) the caches hold E4M3 codes (one-byte layouts)."""
+    if fp8_scales is None:
+        ks = [k_rows(k_cache_bits, page_row, positions, g) for g in range(G)]
+        vs = [v_rows(v_cache_bits, page_row, positions, g) for g in range(G)]
+    else:
+        ks = [k_rows_fp8(k_cache_bits, page_row, positions, g, fp8_scales[0]) for g in range(G)]
+        vs = [v_rows_fp8(v_cache_bits, page_row, positions, g, fp8_scales[1]) for g in range(G)]
     return attend(q_heads, ks, vs, scale)
 
 
@@ -248,16 +290,16 @@ def sparse_layer_token(q_heads_bits, q_idx_bits, k_cache_bits, v_cache_bits, kid
     return sel, O, lse
 
 
-def sparse_attention_token(q_heads_bits, k_cache_bits, v_cache_bits, page_row, sel, p, scale):
+def sparse_attention_token(q_heads_bits, k_cache_bits, v_cache_bits, page_row, sel, p, scale, fp8_scales=None):
     """Attention of one query token given its selected blocks."""
     pos = sparse_token_positions(np.asarray(sel), p)
     return attend_positions(bf16_to_f64(q_heads_bits), k_cache_bits, v_cache_bits,
-                            page_row, pos, scale)
+                            page_row, pos, scale, fp8_scales)
 
 
 def swa_token(q_heads_bits, k_cache_bits, v_cache_bits, page_row, p: int, window: int,
-              scale: float):
+              scale: float, fp8_scales=None):
     """Sliding-window attention of one query token."""
     pos = window_positions(p, window)
     return attend_positions(bf16_to_f64(q_heads_bits), k_cache_bits, v_cache_bits,
-                            page_row, pos, scale)
+                            page_row, pos, scale, fp8_scales)

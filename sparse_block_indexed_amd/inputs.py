@@ -215,6 +215,50 @@ def fp8_e4m3_codes(t: torch.Tensor) -> torch.Tensor:
     return t.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+FP8_UNIT = BS * D   # bytes in one (page, group, block) unit of a one-byte K or V cache
+
+
+def quantize_kv_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float, v_scale: float,
+                    chunk_pages: int = 2048):
+    """One-byte (OCP E4M3) copies of bf16 K/V caches: code = round(x / scale).
+
+    K goes from the bf16 layout [page][group][block][24 chunks][8 tokens][8 dims]
+    to the one-byte layout [page][group][block][8 tokens][192 dims]; V keeps its
+    [192 dims][8 tokens] order. Returns uint8 tensors [num_pages][4][8][1536]."""
+    P = k_cache.shape[0]
+    kq = torch.empty((P, G, BPP, FP8_UNIT), dtype=torch.uint8, device=k_cache.device)
+    vq = torch.empty_like(kq)
+    for p0 in range(0, P, chunk_pages):
+        p1 = min(P, p0 + chunk_pages)
+        k = k_cache[p0:p1].view(p1 - p0, G, BPP, D // 8, BS, 8).permute(0, 1, 2, 4, 3, 5)
+        k = k.reshape(p1 - p0, G, BPP, FP8_UNIT).float() / k_scale
+        kq[p0:p1] = k.to(torch.float8_e4m3fn).view(torch.uint8)
+        v = v_cache[p0:p1].float() / v_scale
+        vq[p0:p1] = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    return kq, vq
+
+
+def pack_k_rows_fp8(k_codes: torch.Tensor, page_row: np.ndarray, positions, g: int, rows: torch.Tensor) -> None:
+    """Store one-byte K rows (uint8 codes, 192 each) in the one-byte K layout."""
+    flat = k_codes.view(-1)
+    for i, pos in enumerate(positions):
+        page = int(page_row[pos // PS])
+        r = pos % PS
+        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT + (r % BS) * D
+        flat[base:base + D] = rows[i].to(flat.device)
+
+
+def pack_v_rows_fp8(v_codes: torch.Tensor, page_row: np.ndarray, positions, g: int, rows: torch.Tensor) -> None:
+    """Store one-byte V rows (uint8 codes, 192 each) in the one-byte V layout."""
+    flat = v_codes.view(-1)
+    for i, pos in enumerate(positions):
+        page = int(page_row[pos // PS])
+        r = pos % PS
+        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT
+        idx = base + torch.arange(D) * BS + (r % BS)
+        flat[idx.to(flat.device)] = rows[i].to(flat.device)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor as a numpy uint16 array (host copy)."""
     assert t.dtype == torch.bfloat16

@@ -375,3 +375,64 @@ def test_fp8_keys_give_the_bf16_selection_for_small_integers():
     k_f8 = O.index_keys(f8, page_row, 20, fp8=True)
     np.testing.assert_array_equal(k_bf, k_f8)
     np.testing.assert_array_equal(k_f8[9], ints[0, 1])      # block 9 = logical page 1 -> physical 0, block 1
+
+
+# ---------------------------------------------------------------------------
+# One-byte K/V caches
+# ---------------------------------------------------------------------------
+
+def test_fp8_kv_layout_hand_offsets_and_packer():
+    num_pages = 3
+    k = torch.zeros(num_pages, 4, 8, 1536, dtype=torch.uint8)
+    v = torch.zeros_like(k)
+    page_row = np.array([2, 0, 1])
+    # hand offsets: K (page 1, group 3, position 70 -> logical page 1 = physical 0, block 0, token 6, dim 100)
+    kf = k.view(-1).numpy()
+    kf[((0 * 4 + 3) * 8 + 0) * 1536 + 6 * 192 + 100] = 0x38            # 1.0
+    vf = v.view(-1).numpy()
+    vf[((0 * 4 + 3) * 8 + 0) * 1536 + 100 * 8 + 6] = 0xC0              # -2.0
+    kr = O.k_rows_fp8(kf, page_row, [70], 3, 0.5)
+    vr = O.v_rows_fp8(vf, page_row, [70], 3, 0.25)
+    assert kr[0, 100] == 0.5 and np.count_nonzero(kr) == 1
+    assert vr[0, 100] == -0.5 and np.count_nonzero(vr) == 1
+    # packer round trip
+    gen = torch.Generator().manual_seed(3)
+    positions = [0, 7, 64, 100, 191]
+    for g in range(4):
+        rk = torch.randint(0, 0x7E, (len(positions), 192), generator=gen).to(torch.uint8)
+        rv = torch.randint(0x80, 0xFE, (len(positions), 192), generator=gen).to(torch.uint8)
+        I.pack_k_rows_fp8(k, page_row, positions, g, rk)
+        I.pack_v_rows_fp8(v, page_row, positions, g, rv)
+        np.testing.assert_array_equal(O.k_rows_fp8(k.numpy(), page_row, positions, g, 2.0),
+                                      O.fp8_e4m3_to_f64(rk.numpy()) * 2.0)
+        np.testing.assert_array_equal(O.v_rows_fp8(v.numpy(), page_row, positions, g, 3.0),
+                                      O.fp8_e4m3_to_f64(rv.numpy()) * 3.0)
+
+
+def test_quantize_kv_fp8_matches_the_rows():
+    """The one-byte caches hold the E4M3 codes of K/V divided by the scale, in
+    the one-byte layouts (checked through both accessors)."""
+    page_row, dk, dv, q, kc, vc = _dense_seq(200, seed=12)
+    kq, vq = I.quantize_kv_fp8(kc, vc, 1 / 32, 1 / 16)
+    pos = list(range(200))
+    for g in range(4):
+        want_k = (dk[g].float() * 32).to(torch.float8_e4m3fn).double().numpy() / 32
+        want_v = (dv[g].float() * 16).to(torch.float8_e4m3fn).double().numpy() / 16
+        np.testing.assert_array_equal(O.k_rows_fp8(kq.numpy(), page_row, pos, g, 1 / 32), want_k)
+        np.testing.assert_array_equal(O.v_rows_fp8(vq.numpy(), page_row, pos, g, 1 / 16), want_v)
+
+
+@pytest.mark.parametrize("seq_len", [9, 700, 4103])
+def test_fp8_kv_attention_equals_sdpa_on_decoded_rows(seq_len):
+    page_row, dk, dv, q, kc, vc = _dense_seq(seq_len, seed=30 + seq_len)
+    ks, vs = 1 / 32, 1 / 16
+    kq, vq = I.quantize_kv_fp8(kc, vc, ks, vs)
+    p = seq_len - 1
+    sel = np.arange(min(512, p // 8))
+    sel = np.concatenate([sel, -np.ones(512 - len(sel), dtype=np.int64)])
+    out, _ = O.sparse_attention_token(I.bf16_bits(q), kq.numpy(), vq.numpy(), page_row, sel, p, SCALE,
+                                      fp8_scales=(ks, vs))
+    dk8 = (dk.float() / ks).to(torch.float8_e4m3fn).double() * ks
+    dv8 = (dv.float() / vs).to(torch.float8_e4m3fn).double() * vs
+    ref = _sdpa(q, dk8, dv8, list(range(p + 1)))
+    np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
