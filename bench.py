@@ -60,9 +60,10 @@ def counter_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: int = 64):
+def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: int = 64, kv_fp8=None):
     """The fp64 oracle timed on this host over a bounded sample of the same
-    workload: whole sequences' query tokens, until the budget is spent."""
+    workload: whole sequences' query tokens, until the budget is spent.
+    kv_fp8 = (k_codes, v_codes, k_scale, v_scale) times the one-byte form."""
     import torch
     from oracle import sa_oracle as O
     from sparse_block_indexed_amd import inputs as I
@@ -95,7 +96,12 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
                 pages |= set(range(max(0, p - window + 1) // 64, p // 64 + 1))
         logical = np.array(sorted(pages), dtype=np.int64)
         idx = torch.as_tensor(row[logical].astype(np.int64), device=dev)
-        kc, vc = I.bf16_bits(wl.k_cache.index_select(0, idx)), I.bf16_bits(wl.v_cache.index_select(0, idx))
+        if kv_fp8 is None:
+            kc, vc = I.bf16_bits(wl.k_cache.index_select(0, idx)), I.bf16_bits(wl.v_cache.index_select(0, idx))
+            fp8_scales = None
+        else:
+            kc, vc = (kv_fp8[0].index_select(0, idx).cpu().numpy(), kv_fp8[1].index_select(0, idx).cpu().numpy())
+            fp8_scales = (kv_fp8[2], kv_fp8[3])
         compact = np.full(row.shape[0], -1, dtype=np.int64)
         compact[logical] = np.arange(len(logical))
         qb = [I.bf16_bits(wl.q[t]) for t in toks]
@@ -109,7 +115,7 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
                 pos = O.sparse_token_positions(sel, p)
             else:
                 pos = O.window_positions(p, window)
-            O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, pos, SCALE)
+            O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, pos, SCALE, fp8_scales=fp8_scales)
             done += 1
             if time.perf_counter() - t0 + t_cpu >= budget_s:
                 break
@@ -137,6 +143,9 @@ def main():
                     help="partitions per (token, group) for the attention call; 0 lets the library pick")
     ap.add_argument("--fp8-index-keys", action="store_true",
                     help="score one-byte (OCP E4M3) index keys: the same integer values, half the bytes")
+    ap.add_argument("--fp8-kv", action="store_true",
+                    help="attend one-byte (OCP E4M3) K/V caches quantised from the bf16 ones "
+                         "(k_scale 1/32, v_scale 1/16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
     args = ap.parse_args()
@@ -168,6 +177,12 @@ def main():
     wl = I.config_workload(W, device=dev)
     pt, sl, qs, qp = wl.device_ints(dev)
     kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if args.fp8_index_keys else wl.k_idx_cache
+    if args.fp8_kv:
+        k_scale, v_scale = 1.0 / 32, 1.0 / 16
+        kc, vc = I.quantize_kv_fp8(wl.k_cache, wl.v_cache, k_scale, v_scale)
+        kv_kw = dict(k_scale=k_scale, v_scale=v_scale)
+    else:
+        kc, vc, kv_kw = wl.k_cache, wl.v_cache, {}
     topk = 512
     window = 512 if W == 2 else None
     n_tok = wl.n_tok
@@ -190,11 +205,11 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if window is None:
-            ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=S, out=out,
-                              out_lse=lse, part_o=part_o, part_lse=part_lse)
+            ops.sparse_decode(wl.q, kc, vc, pt, sl, qs, qp, sel, SCALE, num_splits=S, out=out,
+                              out_lse=lse, part_o=part_o, part_lse=part_lse, **kv_kw)
         else:
-            ops.swa_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, window, SCALE, num_splits=S, out=out,
-                           out_lse=lse, part_o=part_o, part_lse=part_lse)
+            ops.swa_decode(wl.q, kc, vc, pt, sl, qs, qp, window, SCALE, num_splits=S, out=out,
+                           out_lse=lse, part_o=part_o, part_lse=part_lse, **kv_kw)
         if ev is not None:
             ev[2].record(stream)
 
@@ -228,13 +243,14 @@ def main():
         del flush
 
     sel_host = sel.cpu().numpy() if window is None else None
+    kvb = 1 if args.fp8_kv else 2
     if window is None:
-        attn_bytes = B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host)
+        attn_bytes = B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host, kv_bytes=kvb)
         idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk, key_bytes=1 if args.fp8_index_keys else 2)
         attn_flops = B.sparse_attention_flops(wl.q_pos, sel_host)
         idx_flops = B.indexer_flops(wl.q_pos)
     else:
-        attn_bytes = B.swa_attention_bytes(wl.q_seq, wl.q_pos, window)
+        attn_bytes = B.swa_attention_bytes(wl.q_seq, wl.q_pos, window, kv_bytes=kvb)
         idx_bytes, idx_flops = 0, 0
         attn_flops = B.swa_attention_flops(wl.q_pos, window)
     names = {0: "decode_8k_b1", 1: "mtp_verify_128k_b64", 2: "swa_decode_32k_b64", 3: "decode_1m_b4",
@@ -243,13 +259,15 @@ def main():
               "context": (f"uniform [{wl.spec.seq_len_range[0]}, {wl.spec.seq_len_range[1]}]"
                           if wl.spec.seq_len_range else str(sorted(set(int(x) for x in wl.seq_lens)))),
               "block_tokens": 8, "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S}
+    config["kv_cache"] = "fp8_e4m3" if args.fp8_kv else "bf16"
     if window is None:
         config["topk_blocks"] = topk
         config["index_keys"] = "fp8_e4m3" if args.fp8_index_keys else "bf16"
     else:
         config["window"] = window
-    metric = METRIC if (W == 1 and not args.fp8_index_keys) else \
-        f"{names[W]}{' (fp8 index keys)' if args.fp8_index_keys else ''} query-tokens/s; achieved HBM GB/s"
+    tags = [t for t, on in (("fp8 index keys", args.fp8_index_keys), ("fp8 KV", args.fp8_kv)) if on]
+    metric = METRIC if (W == 1 and not tags) else \
+        f"{names[W]}{' (' + ', '.join(tags) + ')' if tags else ''} query-tokens/s; achieved HBM GB/s"
     result = {
         "metric": metric,
         "value": n_tok / (ms_per_step * 1e-3),
@@ -270,7 +288,9 @@ def main():
         "algorithmic_bytes": {"indexer_topk": idx_bytes, ("swa_decode" if window else "sparse_decode"): attn_bytes},
         "algorithmic_flops": {"indexer_topk": idx_flops, ("swa_decode" if window else "sparse_decode"): attn_flops},
     }
-    kname = "attention_kernel<%s> (%s)" % (("true", "sa_swa_decode") if window else ("false", "sa_sparse_decode"))
+    kname = "attention_kernel<%s, %s> (%s%s)" % ("true" if window else "false", "fp8" if args.fp8_kv else "bf16",
+                                                 "sa_swa_decode" if window else "sa_sparse_decode",
+                                                 "_fp8kv" if args.fp8_kv else "")
     if W == 4:
         # the prefill chunk is a dense-contraction workload on paper: report MFMA utilisation
         tf = (attn_flops + idx_flops) / (ms_per_step * 1e-3) / 1e12
@@ -288,12 +308,15 @@ def main():
         achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                               "frac": achieved / PEAK_HBM_GBPS,
-                              "traffic": counter_traffic() if W == 1 else None, "kernel": kname}
+                              "traffic": counter_traffic() if (W == 1 and not args.fp8_kv) else None,
+                              "kernel": kname}
     if cold_ms is not None:
         result["cold_cache"] = {"ms_per_step": cold_ms, "attention_ms": cold_attn_ms,
                                 "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, sel_host, window)
+        result["cpu_baseline"] = cpu_baseline(wl, sel_host, window,
+                                              kv_fp8=(kc, vc, kv_kw["k_scale"], kv_kw["v_scale"])
+                                              if args.fp8_kv else None)
     print(json.dumps(result), flush=True)
 
 

@@ -35,6 +35,10 @@
  * - K cache  bf16 [num_pages][4 groups][8 blocks][24 dim-chunks][8 tokens][8 dims]
  * - V cache  bf16 [num_pages][4 groups][8 blocks][192 dims][8 tokens]
  * - index-key cache bf16 [num_pages][8 blocks][256]
+ * One-byte (OCP FP8 E4M3) forms, same page / block addressing:
+ * - K cache  uint8 [num_pages][4 groups][8 blocks][8 tokens][192 dims]
+ * - V cache  uint8 [num_pages][4 groups][8 blocks][192 dims][8 tokens]
+ * - index-key cache uint8 [num_pages][8 blocks][256]
  *   Token position p of sequence b lives in physical page page_table[b][p / 64],
  *   block (p % 64) / 8 of that page, token p % 8 of that block.
  */
@@ -172,6 +176,33 @@ sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
                         int n_tok, int window, float softmax_scale, int num_splits,
                         float* part_o, float* part_lse, void* out, float* out_lse,
                         hipStream_t stream);
+
+/*
+ * sa_sparse_decode and sa_swa_decode over one-byte K/V caches. (Open-weights
+ * blog, "Fitting it on a node": serving stacks may keep the KV of the
+ * full-attention layers in FP8, at some loss of accuracy; one byte per value
+ * halves what every decode step gathers. The window form is offered alongside.)
+ *
+ * k_cache_fp8, v_cache_fp8  device uint8, the one-byte layouts above, OCP FP8
+ *              E4M3 codes (bias 7, no infinities, S.1111.111 is NaN).
+ * k_scale, v_scale  per-cache dequantisation scales: the attended key is
+ *              code * k_scale and the value code * v_scale; both must be finite
+ *              and > 0 (else SA_ERR_INVALID_ARG).
+ * Every other argument and every output is as for the bf16 entry point; codes
+ * are widened exactly to bf16, so K and V enter the products unrounded.
+ */
+sa_status sa_sparse_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8,
+                                 float k_scale, float v_scale, sa_paged_desc pd,
+                                 const int32_t* q_seq, const int32_t* q_pos, const int32_t* sel_idx,
+                                 int n_tok, int topk, float softmax_scale, int num_splits,
+                                 float* part_o, float* part_lse, void* out, float* out_lse,
+                                 hipStream_t stream);
+
+sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8,
+                              float k_scale, float v_scale, sa_paged_desc pd,
+                              const int32_t* q_seq, const int32_t* q_pos, int n_tok, int window,
+                              float softmax_scale, int num_splits, float* part_o, float* part_lse,
+                              void* out, float* out_lse, hipStream_t stream);
 
 /*
  * Merge of per-partition results (SGLang blog, "Kernels from StepFun").

@@ -73,9 +73,9 @@ def unique_kv_units(q_seq, q_pos, blocks_of_token) -> int:
 
 
 def sparse_attention_bytes(q_seq, q_pos, sel_idx: np.ndarray, num_heads: int = H,
-                           write_lse: bool = True) -> int:
+                           write_lse: bool = True, kv_bytes: int = BF16) -> int:
     """Distinct K and V units of the selected + current blocks (all 4 groups), Q read,
-    O written (bf16), selection read, lse written."""
+    O written (bf16), selection read, lse written. kv_bytes = 1 for one-byte caches."""
     sel_idx = np.asarray(sel_idx)
     n_tok = len(q_seq)
 
@@ -84,7 +84,7 @@ def sparse_attention_bytes(q_seq, q_pos, sel_idx: np.ndarray, num_heads: int = H
         return list(s[s >= 0]) + [int(q_pos[t]) // BS]
 
     units = unique_kv_units(q_seq, q_pos, blocks)
-    total = units * G * 2 * UNIT_BYTES
+    total = units * G * 2 * BS * D * kv_bytes
     total += n_tok * num_heads * D * BF16 * 2       # Q in, O out
     total += sel_idx.size * 4
     if write_lse:
@@ -92,7 +92,8 @@ def sparse_attention_bytes(q_seq, q_pos, sel_idx: np.ndarray, num_heads: int = H
     return total
 
 
-def swa_attention_bytes(q_seq, q_pos, window: int, num_heads: int = H, write_lse: bool = True) -> int:
+def swa_attention_bytes(q_seq, q_pos, window: int, num_heads: int = H, write_lse: bool = True,
+                        kv_bytes: int = BF16) -> int:
     """Distinct K and V blocks touched by the windows, Q read, O written."""
     def blocks(t):
         p = int(q_pos[t])
@@ -101,7 +102,7 @@ def swa_attention_bytes(q_seq, q_pos, window: int, num_heads: int = H, write_lse
 
     units = unique_kv_units(q_seq, q_pos, blocks)
     n_tok = len(q_seq)
-    total = units * G * 2 * UNIT_BYTES + n_tok * num_heads * D * BF16 * 2
+    total = units * G * 2 * BS * D * kv_bytes + n_tok * num_heads * D * BF16 * 2
     if write_lse:
         total += n_tok * num_heads * 4
     return total

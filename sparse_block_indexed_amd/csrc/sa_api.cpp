@@ -33,9 +33,10 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* q_seq, const int32_t* q_pos, int n_tok, float softmax_scale,
                         int max_blocks, int num_splits, float* part_o, float* part_lse, void* out,
                         float* out_lse, bool window_mode, const int32_t* sel_idx, int topk, int window,
-                        hipStream_t stream) {
+                        bool kv_fp8, float k_scale, float v_scale, hipStream_t stream) {
   if (n_tok < 0 || num_splits < 0) return SA_ERR_INVALID_ARG;
   if (n_tok == 0) return SA_OK;
+  if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return SA_ERR_INVALID_ARG;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr) return SA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return SA_ERR_INVALID_ARG;
   sa_status st = check_desc(pd);
@@ -67,7 +68,11 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   a.batch = pd.batch;
   a.max_pages = pd.max_pages_per_seq;
   a.num_pages = pd.num_pages;
-  a.scale_log2 = softmax_scale * kLog2e;
+  // A one-byte cache stores K / k_scale: the scale joins the logit scale.
+  a.scale_log2 = softmax_scale * k_scale * kLog2e;
+  if (!isfinite(a.scale_log2)) return SA_ERR_INVALID_ARG;
+  a.kv_fp8 = kv_fp8;
+  a.v_scale = v_scale;
   // Many query tokens per sequence (a prefill chunk) re-read the same blocks:
   // keep them cacheable then; decode-like calls stream them.
   a.stream_kv = n_tok <= 64 * pd.batch;
@@ -194,7 +199,19 @@ sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cac
     if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
   }
   return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
-                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, stream);
+                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, false, 1.f, 1.f, stream);
+}
+
+sa_status sa_sparse_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8, float k_scale,
+                                 float v_scale, sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
+                                 const int32_t* sel_idx, int n_tok, int topk, float softmax_scale, int num_splits,
+                                 float* part_o, float* part_lse, void* out, float* out_lse, hipStream_t stream) {
+  if (n_tok > 0) {
+    if (sel_idx == nullptr || !aligned(sel_idx, 4)) return SA_ERR_INVALID_ARG;
+    if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
+  }
+  return decode_common(q, k_cache_fp8, v_cache_fp8, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
+                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, true, k_scale, v_scale, stream);
 }
 
 sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,
@@ -203,7 +220,17 @@ sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
                         hipStream_t stream) {
   if (n_tok > 0 && (window < 1 || window > SA_MAX_WINDOW)) return SA_ERR_UNSUPPORTED;
   return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, window / 8 + 2, num_splits,
-                       part_o, part_lse, out, out_lse, true, nullptr, 0, window, stream);
+                       part_o, part_lse, out, out_lse, true, nullptr, 0, window, false, 1.f, 1.f, stream);
+}
+
+sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8, float k_scale,
+                              float v_scale, sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
+                              int n_tok, int window, float softmax_scale, int num_splits, float* part_o,
+                              float* part_lse, void* out, float* out_lse, hipStream_t stream) {
+  if (n_tok > 0 && (window < 1 || window > SA_MAX_WINDOW)) return SA_ERR_UNSUPPORTED;
+  return decode_common(q, k_cache_fp8, v_cache_fp8, pd, q_seq, q_pos, n_tok, softmax_scale, window / 8 + 2,
+                       num_splits, part_o, part_lse, out, out_lse, true, nullptr, 0, window, true, k_scale, v_scale,
+                       stream);
 }
 
 sa_status sa_merge(const float* part_o, const float* part_lse, int n_tok, int num_splits, int num_heads,

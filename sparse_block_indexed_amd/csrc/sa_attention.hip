@@ -39,6 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -69,8 +70,28 @@ __device__ __forceinline__ u32x4 load16_kv(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <bool kWindow, bool kStream>
+template <bool kStream>
+__device__ __forceinline__ u32x2 load8_kv(const uint8_t* p) {
+  if constexpr (kStream) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// Eight OCP E4M3 bytes (two words) to eight bf16 (an MFMA operand); exact.
+template <bool kHiHalf>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHiHalf));
+}
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+               fp8x2_to_bf16x2<true>(w1)};
+}
+
+// kFp8: one-byte caches. A K unit is [8 tokens][192 dims] (a lane's 48 dims of
+// a token are 48 contiguous bytes), a V unit [192 dims][8 tokens] (8 bytes per
+// dim); both are widened to bf16 right before their MFMA.
+template <bool kWindow, bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
+  constexpr int kUnit = kFp8 ? kUnitBytes / 2 : kUnitBytes;
   __shared__ int32_t s_unit[kMaxSlots];
   __shared__ int32_t s_beta[kMaxSlots];
   __shared__ float s_m[kWaves][16];
@@ -155,13 +176,16 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 12; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K lane offset inside a unit: dim chunk 6*lg (+i), token (lq & 3) (+4 for half 1)
-  const uint8_t* kbase = a.k_cache + lg * 6 * 128 + (lq & 3) * 16;
+  // K lane offset inside a unit: bf16: dim chunk 6*lg (+i), token (lq & 3) (+4 for
+  // half 1); fp8: token (lq & 3) (+4 for half 1), dims 48*lg .. 48*lg+47
+  const uint8_t* kbase = kFp8 ? a.k_cache + (lq & 3) * kHeadDim + lg * 48 : a.k_cache + lg * 6 * 128 + (lq & 3) * 16;
   // V lane offset inside a unit: dim lq (+16 per output tile), all 8 tokens
-  const uint8_t* vbase = a.v_cache + lq * 16;
+  const uint8_t* vbase = a.v_cache + lq * (kFp8 ? 8 : 16);
 
-  u32x4 kr[2][6];
-  u32x4 vr[12];
+  u32x4 kr[2][6];      // bf16 K operands
+  u32x4 vr[12];        // bf16 V operands
+  u32x4 kq[2][3];      // fp8 K bytes (48 per half)
+  u32x2 vq[12];        // fp8 V bytes (8 tokens of one dim)
 
   // Loads are branch-free so that the compiler's waits stay precise: a slot
   // with nothing to read (padding, unreadable page) reads unit 0 instead, and
@@ -169,19 +193,41 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   auto load_k = [&](int c) {
     const int slot = 4 * c + (lq >> 2);
     const int unit = slot < n ? max(s_unit[slot], 0) : 0;
-    const uint8_t* pk = kbase + (size_t)unit * kUnitBytes;
+    const uint8_t* pk = kbase + (size_t)unit * kUnit;
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      kr[0][i] = load16_kv<kStream>(pk + i * 128);
-      kr[1][i] = load16_kv<kStream>(pk + i * 128 + 64);
+      for (int j = 0; j < 3; ++j) {
+        kq[0][j] = load16_kv<kStream>(pk + j * 16);
+        kq[1][j] = load16_kv<kStream>(pk + 4 * kHeadDim + j * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        kr[0][i] = load16_kv<kStream>(pk + i * 128);
+        kr[1][i] = load16_kv<kStream>(pk + i * 128 + 64);
+      }
     }
   };
   auto load_v = [&](int c) {
     const int slot = 4 * c + lg;
     const int unit = slot < n ? max(s_unit[slot], 0) : 0;
-    const uint8_t* pv = vbase + (size_t)unit * kUnitBytes;
+    const uint8_t* pv = vbase + (size_t)unit * kUnit;
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int i = 0; i < 12; ++i) vr[i] = load16_kv<kStream>(pv + i * 256);
+      for (int i = 0; i < 12; ++i) vq[i] = load8_kv<kStream>(pv + i * 128);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 12; ++i) vr[i] = load16_kv<kStream>(pv + i * 256);
+    }
+  };
+  // K operand of half s, k-step i (dims 48*lg + 8i .. +8)
+  auto k_operand = [&](int s, int i) -> u32x4 {
+    if constexpr (kFp8) {
+      const u32x4 w = kq[s][i >> 1];
+      return (i & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+    } else {
+      return kr[s][i];
+    }
   };
 
   // Chunks of this wave: wave, wave + 4, ... The next chunk's K is issued
@@ -198,8 +244,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
-      st0 = mfma_bf16(kr[0][i], qv[i], st0);
-      st1 = mfma_bf16(kr[1][i], qv[i], st1);
+      st0 = mfma_bf16(k_operand(0, i), qv[i], st0);
+      st1 = mfma_bf16(k_operand(1, i), qv[i], st1);
     }
     // keep the refill below the MFMAs that read kr: hoisting it would need a
     // second set of K registers
@@ -255,6 +301,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     // window's first block before lo, slots that read unit 0 as a stand-in)
     // may hold anything; zero their V so that a zero probability never meets a
     // non-finite value.
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int i = 0; i < 12; ++i) vr[i] = fp8x8_to_bf16x8(vq[i].x, vq[i].y);
+    }
     if (__any(okmask != 0xffu)) {
       u32x4 vm;
 #pragma unroll
@@ -308,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     for (int i = 0; i < 12; ++i) acc[i] += s_o[w - 1][i][lane] * aw;
   }
   const bool any = L > 0.f;
-  const float inv = any ? 1.0f / L : 0.f;
+  const float inv = any ? a.v_scale / L : 0.f;   // V scale of a one-byte cache (1 for bf16)
   const float lse = any ? (M + __builtin_amdgcn_logf(E)) * kLn2 : -INFINITY;
   const int head = g * kHeadsPerGroup + lq;
 
@@ -336,13 +386,19 @@ hipError_t launch_attention(const AttnArgs& a, bool window_mode, hipStream_t str
   if (a.n_tok == 0) return hipSuccess;
   const long long grid = (long long)a.n_tok * kGroups * a.num_splits;
   const dim3 g((unsigned)grid), b(kThreads);
+#define SA_ATTN(W, F)                                                         \
+  do {                                                                        \
+    if (a.stream_kv) attention_kernel<W, true, F><<<g, b, 0, stream>>>(a);    \
+    else attention_kernel<W, false, F><<<g, b, 0, stream>>>(a);               \
+  } while (0)
   if (window_mode) {
-    if (a.stream_kv) attention_kernel<true, true><<<g, b, 0, stream>>>(a);
-    else attention_kernel<true, false><<<g, b, 0, stream>>>(a);
+    if (a.kv_fp8) SA_ATTN(true, true);
+    else SA_ATTN(true, false);
   } else {
-    if (a.stream_kv) attention_kernel<false, true><<<g, b, 0, stream>>>(a);
-    else attention_kernel<false, false><<<g, b, 0, stream>>>(a);
+    if (a.kv_fp8) SA_ATTN(false, true);
+    else SA_ATTN(false, false);
   }
+#undef SA_ATTN
   return hipGetLastError();
 }
 

@@ -45,6 +45,8 @@ struct AttnArgs {
   int num_pages;
   float scale_log2;         // softmax_scale * log2(e)
   bool stream_kv;           // non-temporal K/V loads (blocks read about once per call)
+  bool kv_fp8;              // one-byte (OCP E4M3) K/V caches
+  float v_scale;            // V = code * v_scale for a one-byte cache (1 for bf16)
   float* part_o;            // used when num_splits > 1
   float* part_lse;
   uint16_t* out;            // used when num_splits == 1

@@ -22,7 +22,8 @@ MAX_SPLITS = 64
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 EXPORTED = ["sa_status_string", "sa_indexer_topk_workspace_size", "sa_indexer_topk", "sa_indexer_topk_fp8",
-            "sa_resolve_num_splits", "sa_sparse_decode", "sa_swa_decode", "sa_merge"]
+            "sa_resolve_num_splits", "sa_sparse_decode", "sa_sparse_decode_fp8kv", "sa_swa_decode",
+            "sa_swa_decode_fp8kv", "sa_merge"]
 
 
 class SAError(RuntimeError):
@@ -62,6 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sa_sparse_decode.argtypes = [vp, vp, vp, PagedDesc, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp]
     lib.sa_swa_decode.restype = i32
     lib.sa_swa_decode.argtypes = [vp, vp, vp, PagedDesc, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp]
+    lib.sa_sparse_decode_fp8kv.restype = i32
+    lib.sa_sparse_decode_fp8kv.argtypes = [vp, vp, vp, f32, f32, PagedDesc, vp, vp, vp, i32, i32, f32, i32, vp, vp,
+                                           vp, vp, vp]
+    lib.sa_swa_decode_fp8kv.restype = i32
+    lib.sa_swa_decode_fp8kv.argtypes = [vp, vp, vp, f32, f32, PagedDesc, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp,
+                                        vp]
     lib.sa_merge.restype = i32
     lib.sa_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     _lib = lib
@@ -160,55 +167,86 @@ def _decode_buffers(n_tok, S, dev, out, out_lse, part_o, part_lse, want_out=True
     return out, out_lse, part_o, part_lse
 
 
-def _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos):
+def _is_fp8(t) -> bool:
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
+def _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos, k_scale, v_scale):
+    """Checks shapes and dtypes; returns (dev, n_tok, fp8, k_cache, v_cache).
+
+    Caches are both bf16, or both one-byte E4M3 (float8_e4m3fn or uint8 codes,
+    returned as uint8 views), which need k_scale and v_scale."""
     dev = q.device
     n_tok = q.shape[0]
     _need(q, "q", torch.bfloat16, dev, (n_tok, H, D))
+    fp8 = _is_fp8(k_cache)
+    if fp8 != _is_fp8(v_cache):
+        raise ValueError("k_cache and v_cache must both be bf16 or both one-byte")
+    if fp8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("one-byte caches need k_scale and v_scale")
+        k_cache, v_cache = k_cache.view(torch.uint8), v_cache.view(torch.uint8)
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale / v_scale apply to one-byte caches only")
     for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _need(c, name, torch.bfloat16, dev)
+        _need(c, name, torch.uint8 if fp8 else torch.bfloat16, dev)
         if c.dim() != 4 or tuple(c.shape[1:]) != (G, 8, 8 * D):
             raise ValueError(f"{name}: expected [num_pages][4][8][1536]")
     if k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache differ in shape")
     _need(q_seq, "q_seq", torch.int32, dev, (n_tok,))
     _need(q_pos, "q_pos", torch.int32, dev, (n_tok,))
-    return dev, n_tok
+    return dev, n_tok, fp8, k_cache, v_cache
 
 
 def sparse_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, sel_idx, softmax_scale: float,
                   num_splits: int = 0, out=None, out_lse=None, part_o=None, part_lse=None,
-                  partials_only: bool = False, stream=None):
+                  partials_only: bool = False, stream=None, k_scale: Optional[float] = None,
+                  v_scale: Optional[float] = None):
     """Attention over selected + current blocks. Returns (out, out_lse) or, with
-    partials_only, (part_o, part_lse) of the resolved number of splits."""
+    partials_only, (part_o, part_lse) of the resolved number of splits. One-byte
+    caches (with k_scale, v_scale) go to sa_sparse_decode_fp8kv."""
     lib = load_library()
-    dev, n_tok = _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos)
+    dev, n_tok, fp8, k_cache, v_cache = _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos, k_scale, v_scale)
     topk = sel_idx.shape[1]
     _need(sel_idx, "sel_idx", torch.int32, dev, (n_tok, topk))
     pd = _desc(page_table, seq_lens, k_cache.shape[0])
     S = resolve_num_splits(n_tok, topk + 1, num_splits)
     out, out_lse, part_o, part_lse = _decode_buffers(n_tok, S, dev, out, out_lse, part_o, part_lse,
                                                      want_out=not partials_only)
-    st = lib.sa_sparse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), pd, _ptr(q_seq), _ptr(q_pos), _ptr(sel_idx),
-                              n_tok, topk, float(softmax_scale), int(num_splits), _ptr(part_o), _ptr(part_lse),
-                              None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
-    _check("sa_sparse_decode", st)
+    tail = (pd, _ptr(q_seq), _ptr(q_pos), _ptr(sel_idx), n_tok, topk, float(softmax_scale), int(num_splits),
+            _ptr(part_o), _ptr(part_lse), None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
+    if fp8:
+        name = "sa_sparse_decode_fp8kv"
+        st = lib.sa_sparse_decode_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale), *tail)
+    else:
+        name = "sa_sparse_decode"
+        st = lib.sa_sparse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail)
+    _check(name, st)
     return (part_o, part_lse) if partials_only else (out, out_lse)
 
 
 def swa_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, window: int, softmax_scale: float,
                num_splits: int = 0, out=None, out_lse=None, part_o=None, part_lse=None,
-               partials_only: bool = False, stream=None):
-    """Sliding-window attention over positions max(0, p - window + 1) .. p."""
+               partials_only: bool = False, stream=None, k_scale: Optional[float] = None,
+               v_scale: Optional[float] = None):
+    """Sliding-window attention over positions max(0, p - window + 1) .. p.
+    One-byte caches (with k_scale, v_scale) go to sa_swa_decode_fp8kv."""
     lib = load_library()
-    dev, n_tok = _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos)
+    dev, n_tok, fp8, k_cache, v_cache = _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos, k_scale, v_scale)
     pd = _desc(page_table, seq_lens, k_cache.shape[0])
     S = resolve_num_splits(n_tok, window // 8 + 2, num_splits)
     out, out_lse, part_o, part_lse = _decode_buffers(n_tok, S, dev, out, out_lse, part_o, part_lse,
                                                      want_out=not partials_only)
-    st = lib.sa_swa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), pd, _ptr(q_seq), _ptr(q_pos), n_tok, int(window),
-                           float(softmax_scale), int(num_splits), _ptr(part_o), _ptr(part_lse),
-                           None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
-    _check("sa_swa_decode", st)
+    tail = (pd, _ptr(q_seq), _ptr(q_pos), n_tok, int(window), float(softmax_scale), int(num_splits), _ptr(part_o),
+            _ptr(part_lse), None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
+    if fp8:
+        name = "sa_swa_decode_fp8kv"
+        st = lib.sa_swa_decode_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale), *tail)
+    else:
+        name = "sa_swa_decode"
+        st = lib.sa_swa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail)
+    _check(name, st)
     return (part_o, part_lse) if partials_only else (out, out_lse)
 
 
@@ -231,10 +269,11 @@ def merge(part_o, part_lse, out=None, out_lse=None, stream=None):
 
 
 def sparse_layer(q, q_idx, k_cache, v_cache, k_idx_cache, page_table, seq_lens, q_seq, q_pos,
-                 softmax_scale: float, topk: int = MAX_TOPK, num_splits: int = 0, workspace=None, stream=None):
+                 softmax_scale: float, topk: int = MAX_TOPK, num_splits: int = 0, workspace=None, stream=None,
+                 k_scale: Optional[float] = None, v_scale: Optional[float] = None):
     """The sparse layer's whole decode step: indexer top-k, then attention (+ merge)."""
     sel = indexer_topk(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk, workspace=workspace,
                        stream=stream)
     out, lse = sparse_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, sel, softmax_scale,
-                             num_splits=num_splits, stream=stream)
+                             num_splits=num_splits, stream=stream, k_scale=k_scale, v_scale=v_scale)
     return sel, out, lse

@@ -21,30 +21,44 @@ def device_tables(wl, device="cuda"):
     return wl.device_ints(device)
 
 
-def run_sparse_layer(wl, topk=512, num_splits=0, scale=SCALE, tabs=None, kidx=None):
+def _kv_args(wl, kv_fp8):
+    """(k_cache, v_cache, scale kwargs) of the bf16 caches, or of kv_fp8 =
+    (k_codes, v_codes, k_scale, v_scale)."""
+    if kv_fp8 is None:
+        return wl.k_cache, wl.v_cache, {}
+    kc, vc, ks, vs = kv_fp8
+    return kc, vc, dict(k_scale=ks, v_scale=vs)
+
+
+def run_sparse_layer(wl, topk=512, num_splits=0, scale=SCALE, tabs=None, kidx=None, kv_fp8=None):
     from sparse_block_indexed_amd import ops
     pt, sl, qs, qp = tabs if tabs is not None else device_tables(wl)
     sel = ops.indexer_topk(wl.q_idx, wl.k_idx_cache if kidx is None else kidx, pt, sl, qs, qp, topk)
-    out, lse = ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, scale, num_splits=num_splits)
+    kc, vc, kw = _kv_args(wl, kv_fp8)
+    out, lse = ops.sparse_decode(wl.q, kc, vc, pt, sl, qs, qp, sel, scale, num_splits=num_splits, **kw)
     torch.cuda.synchronize()
     return sel, out, lse
 
 
-def run_swa(wl, window=512, num_splits=0, scale=SCALE, tabs=None):
+def run_swa(wl, window=512, num_splits=0, scale=SCALE, tabs=None, kv_fp8=None):
     from sparse_block_indexed_amd import ops
     pt, sl, qs, qp = tabs if tabs is not None else device_tables(wl)
-    out, lse = ops.swa_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, window, scale, num_splits=num_splits)
+    kc, vc, kw = _kv_args(wl, kv_fp8)
+    out, lse = ops.swa_decode(wl.q, kc, vc, pt, sl, qs, qp, window, scale, num_splits=num_splits, **kw)
     torch.cuda.synchronize()
     return out, lse
 
 
 class OracleView:
     """Host-side oracle over a device workload; caches each sequence's index keys.
-    With kidx_fp8 (uint8 E4M3 codes) the index keys are read from it instead."""
+    With kidx_fp8 (uint8 E4M3 codes) the index keys are read from it instead;
+    with kv_fp8 = (k_codes, v_codes, k_scale, v_scale) the attention reads the
+    one-byte caches."""
 
-    def __init__(self, wl, kidx_fp8=None):
+    def __init__(self, wl, kidx_fp8=None, kv_fp8=None):
         self.wl = wl
         self.kidx_fp8 = kidx_fp8
+        self.kv_fp8 = kv_fp8
         self._keys = {}
 
     def keys(self, b, cb):
@@ -75,11 +89,17 @@ class OracleView:
         phys = row[logical].astype(np.int64)
         dev = wl.k_cache.device
         idx = torch.as_tensor(phys, device=dev)
-        kc = I.bf16_bits(wl.k_cache.index_select(0, idx))
-        vc = I.bf16_bits(wl.v_cache.index_select(0, idx))
         compact = np.full(row.shape[0], -1, dtype=np.int64)
         compact[logical] = np.arange(len(logical))
-        return O.attend_positions(O.bf16_to_f64(I.bf16_bits(wl.q[t])), kc, vc, compact, positions, scale)
+        q = O.bf16_to_f64(I.bf16_bits(wl.q[t]))
+        if self.kv_fp8 is not None:
+            k8, v8, ks, vs = self.kv_fp8
+            kc = k8.index_select(0, idx).cpu().numpy()
+            vc = v8.index_select(0, idx).cpu().numpy()
+            return O.attend_positions(q, kc, vc, compact, positions, scale, fp8_scales=(ks, vs))
+        kc = I.bf16_bits(wl.k_cache.index_select(0, idx))
+        vc = I.bf16_bits(wl.v_cache.index_select(0, idx))
+        return O.attend_positions(q, kc, vc, compact, positions, scale)
 
     def sparse(self, t, sel, scale=SCALE):
         return self.attention(t, O.sparse_token_positions(np.asarray(sel), int(self.wl.q_pos[t])), scale)

@@ -28,8 +28,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ["sa_indexer_topk", "sa_indexer_topk_fp8", "sa_sparse_decode", "sa_swa_decode", "sa_merge",
-              "sa_indexer_topk_workspace_size", "sa_status_string", "sa_resolve_num_splits"]:
+    for n in ["sa_indexer_topk", "sa_indexer_topk_fp8", "sa_sparse_decode", "sa_sparse_decode_fp8kv",
+              "sa_swa_decode", "sa_swa_decode_fp8kv", "sa_merge", "sa_indexer_topk_workspace_size",
+              "sa_status_string", "sa_resolve_num_splits"]:
         assert n in names
 
 
@@ -122,6 +123,53 @@ def test_sparse_decode_validation(lib):
     assert call(out=None) == ops.SA_ERR_INVALID_ARG                    # S == 1 needs out
     assert call(S=4, po=None, pl=P) == ops.SA_ERR_INVALID_ARG         # S > 1 needs partials
     assert call(k=P + 4) == ops.SA_ERR_INVALID_ARG                     # misaligned cache
+
+
+def test_fp8kv_decode_validation(lib):
+    """The one-byte K/V entry points check what the bf16 ones check, plus the scales."""
+    from sparse_block_indexed_amd import ops
+    d = _desc(ops)
+    f = lib.sa_sparse_decode_fp8kv
+    ok = dict(q=P, k=P, v=P, ks=0.03, vs=0.06, qs=P, qp=P, sel=P, n=4, topk=512, sc=0.07, S=1, out=P)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], ctypes.c_float(a["ks"]), ctypes.c_float(a["vs"]), d, a["qs"], a["qp"],
+                 a["sel"], a["n"], a["topk"], ctypes.c_float(a["sc"]), a["S"], None, None, a["out"], None, None)
+
+    assert call(n=0, q=None, k=None, v=None, sel=None, out=None) == ops.SA_OK
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(ks=bad) == ops.SA_ERR_INVALID_ARG
+        assert call(vs=bad) == ops.SA_ERR_INVALID_ARG
+    assert call(ks=1e30, sc=1e30) == ops.SA_ERR_INVALID_ARG          # logit scale overflows fp32
+    assert call(sel=None) == ops.SA_ERR_INVALID_ARG
+    assert call(topk=513) == ops.SA_ERR_UNSUPPORTED
+    assert call(v=P + 8) == ops.SA_ERR_INVALID_ARG
+    w = lib.sa_swa_decode_fp8kv
+    assert w(P, P, P, ctypes.c_float(1.0), ctypes.c_float(1.0), d, P, P, 0, 512, ctypes.c_float(0.1), 0,
+             None, None, None, None, None) == ops.SA_OK
+    assert w(P, P, P, ctypes.c_float(1.0), ctypes.c_float(0.0), d, P, P, 2, 512, ctypes.c_float(0.1), 1,
+             None, None, P, None, None) == ops.SA_ERR_INVALID_ARG
+    assert w(P, P, P, ctypes.c_float(1.0), ctypes.c_float(1.0), d, P, P, 2, 0, ctypes.c_float(0.1), 1,
+             None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
+
+
+def test_binding_checks_fp8_cache_arguments():
+    """The Python binding refuses mixed cache dtypes and missing scales before any call."""
+    import torch
+    from sparse_block_indexed_amd import ops
+    q = torch.zeros(1, 64, 192, dtype=torch.bfloat16)
+    k8 = torch.zeros(1, 4, 8, 1536, dtype=torch.uint8)
+    kb = torch.zeros(1, 4, 8, 1536, dtype=torch.bfloat16)
+    i = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="both"):
+        ops._check_attn_inputs(q, k8, kb, i, i, 1.0, 1.0)
+    with pytest.raises(ValueError, match="need k_scale"):
+        ops._check_attn_inputs(q, k8, k8, i, i, None, 1.0)
+    with pytest.raises(ValueError, match="one-byte caches only"):
+        ops._check_attn_inputs(q, kb, kb, i, i, 1.0, None)
+    dev, n, fp8, k, v = ops._check_attn_inputs(q, k8.view(torch.float8_e4m3fn), k8, i, i, 0.5, 0.25)
+    assert fp8 and n == 1 and k.dtype == torch.uint8 and v.dtype == torch.uint8
 
 
 def test_swa_and_merge_validation(lib):
