@@ -36,7 +36,8 @@
  * - V cache  bf16 [num_pages][4 groups][8 blocks][192 dims][8 tokens]
  * - index-key cache bf16 [num_pages][8 blocks][256]
  * One-byte (OCP FP8 E4M3) forms, same page / block addressing:
- * - K cache  uint8 [num_pages][4 groups][8 blocks][8 tokens][192 dims]
+ * - K cache  uint8 [num_pages][4 groups][8 blocks][3 dim-blocks][8 tokens][64 dims]
+ *   (dim d of a token in dim-block d / 64, at d % 64)
  * - V cache  uint8 [num_pages][4 groups][8 blocks][192 dims][8 tokens]
  * - index-key cache uint8 [num_pages][8 blocks][256]
  *   Token position p of sequence b lives in physical page page_table[b][p / 64],

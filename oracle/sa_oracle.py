@@ -118,9 +118,11 @@ def v_rows(v_cache_bits: np.ndarray, page_row: np.ndarray, positions, g: int) ->
 
 # One-byte (OCP FP8 E4M3) K/V caches: the value is code * scale, with a scale
 # per cache (per layer).  Layouts:
-#   K: [page][group][block-in-page][8 tokens][192 dims]
+#   K: [page][group][block-in-page][3 dim-blocks][8 tokens][64 dims]
+#      (token k, dim d at (d // 64) * 512 + k * 64 + d % 64 inside its block)
 #   V: [page][group][block-in-page][192 dims][8 tokens]
 FP8_UNIT = BS * D
+_K8_DIM_OFFSET = (np.arange(D) // 64) * (BS * 64) + np.arange(D) % 64
 
 
 def k_rows_fp8(k_codes: np.ndarray, page_row: np.ndarray, positions, g: int, k_scale: float) -> np.ndarray:
@@ -130,8 +132,8 @@ def k_rows_fp8(k_codes: np.ndarray, page_row: np.ndarray, positions, g: int, k_s
     for i, pos in enumerate(positions):
         page = int(page_row[pos // PS])
         r = pos % PS
-        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT + (r % BS) * D
-        out[i] = fp8_e4m3_to_f64(flat[base:base + D]) * k_scale
+        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT + (r % BS) * 64
+        out[i] = fp8_e4m3_to_f64(flat[base + _K8_DIM_OFFSET]) * k_scale
     return out
 
 

@@ -23,7 +23,8 @@
 //           A = K rows straight from the cache (16 B per lane per k-step),
 //           B = Q of the 16 heads, loaded once.
 //   output  O^T[dim][head] += V^T[dim][token] . P^T[token][head]
-//           A = V from the cache (the V layout keeps 8 tokens of one dim in 16 B),
+//           A = V from the cache (the V layout keeps 8 tokens of one dim in 16 B,
+//           8 B in the one-byte form),
 //           B = P: each lane already holds the 8 probabilities of "its" block for
 //           "its" head, so no data moves between lanes.
 // Token order inside a chunk is chosen so that the rows of the score half-tiles
@@ -86,9 +87,9 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                fp8x2_to_bf16x2<true>(w1)};
 }
 
-// kFp8: one-byte caches. A K unit is [8 tokens][192 dims] (a lane's 48 dims of
-// a token are 48 contiguous bytes), a V unit [192 dims][8 tokens] (8 bytes per
-// dim); both are widened to bf16 right before their MFMA.
+// kFp8: one-byte caches. A K unit is [3 dim-blocks][8 tokens][64 dims], a V
+// unit [192 dims][8 tokens] (8 bytes per dim); both are widened exactly to bf16
+// right before their MFMA.
 template <bool kWindow, bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   constexpr int kUnit = kFp8 ? kUnitBytes / 2 : kUnitBytes;
@@ -160,12 +161,16 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   __syncthreads();
 
   // ---- per-wave streaming loop -------------------------------------------
-  // Q of head 16g + lq, dim chunks 6*lg .. 6*lg+5 (B operand of the score MFMA)
+  // Q of head 16g + lq (B operand of the score MFMA): k-step i of lane group lg covers dims 64*(i/2) + 16*lg + 8*(i%2) .. +8 (the
+  // order of the one-byte K layout; both cache forms sum in this order)
   u32x4 qv[6];
   {
-    const uint8_t* qrow = a.q + ((size_t)t * kHeads + g * kHeadsPerGroup + lq) * (kHeadDim * 2) + lg * 6 * 16;
+    const uint8_t* qrow = a.q + ((size_t)t * kHeads + g * kHeadsPerGroup + lq) * (kHeadDim * 2);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) qv[i] = valid ? load16(qrow + i * 16) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < 6; ++i) {
+      const int dim0 = 64 * (i >> 1) + 16 * lg + 8 * (i & 1);
+      qv[i] = valid ? load16(qrow + dim0 * 2) : u32x4{0, 0, 0, 0};
+    }
   }
   const float sc = a.scale_log2;
   const int nchunks = (n + 3) >> 2;
@@ -176,16 +181,18 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 12; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K lane offset inside a unit: bf16: dim chunk 6*lg (+i), token (lq & 3) (+4 for
-  // half 1); fp8: token (lq & 3) (+4 for half 1), dims 48*lg .. 48*lg+47
-  const uint8_t* kbase = kFp8 ? a.k_cache + (lq & 3) * kHeadDim + lg * 48 : a.k_cache + lg * 6 * 128 + (lq & 3) * 16;
+  // K lane offset inside a unit: bf16: dim chunk 2*lg (+8*(i/2) + i%2), token
+  // (lq & 3) (+4 for half 1); one-byte: dim-block j (+512 j), token (lq & 3) (+4
+  // for half 1), dims 16*lg .. 16*lg+15 of the block -- each load step reads 256
+  // contiguous bytes of every unit
+  const uint8_t* kbase = kFp8 ? a.k_cache + (lq & 3) * 64 + lg * 16 : a.k_cache + lg * 256 + (lq & 3) * 16;
   // V lane offset inside a unit: dim lq (+16 per output tile), all 8 tokens
   const uint8_t* vbase = a.v_cache + lq * (kFp8 ? 8 : 16);
 
   u32x4 kr[2][6];      // bf16 K operands
   u32x4 vr[12];        // bf16 V operands
-  u32x4 kq[2][3];      // fp8 K bytes (48 per half)
-  u32x2 vq[12];        // fp8 V bytes (8 tokens of one dim)
+  u32x4 kq[2][3];      // one-byte K: 16 dims (two k-steps) per dim-block and half
+  u32x2 vq[12];        // one-byte V: 8 tokens of one dim
 
   // Loads are branch-free so that the compiler's waits stay precise: a slot
   // with nothing to read (padding, unreadable page) reads unit 0 instead, and
@@ -197,14 +204,15 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     if constexpr (kFp8) {
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
-        kq[0][j] = load16_kv<kStream>(pk + j * 16);
-        kq[1][j] = load16_kv<kStream>(pk + 4 * kHeadDim + j * 16);
+        kq[0][j] = load16_kv<kStream>(pk + j * 512);
+        kq[1][j] = load16_kv<kStream>(pk + j * 512 + 256);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 6; ++i) {
-        kr[0][i] = load16_kv<kStream>(pk + i * 128);
-        kr[1][i] = load16_kv<kStream>(pk + i * 128 + 64);
+        const int off = (8 * (i >> 1) + (i & 1)) * 128;
+        kr[0][i] = load16_kv<kStream>(pk + off);
+        kr[1][i] = load16_kv<kStream>(pk + off + 64);
       }
     }
   };
@@ -218,15 +226,6 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < 12; ++i) vr[i] = load16_kv<kStream>(pv + i * 256);
-    }
-  };
-  // K operand of half s, k-step i (dims 48*lg + 8i .. +8)
-  auto k_operand = [&](int s, int i) -> u32x4 {
-    if constexpr (kFp8) {
-      const u32x4 w = kq[s][i >> 1];
-      return (i & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
-    } else {
-      return kr[s][i];
     }
   };
 
@@ -244,11 +243,18 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
-      st0 = mfma_bf16(k_operand(0, i), qv[i], st0);
-      st1 = mfma_bf16(k_operand(1, i), qv[i], st1);
+      if constexpr (kFp8) {
+        const u32x4 w0 = kq[0][i >> 1], w1 = kq[1][i >> 1];
+        const int h = (i & 1) * 2;
+        st0 = mfma_bf16(fp8x8_to_bf16x8(w0[h], w0[h + 1]), qv[i], st0);
+        st1 = mfma_bf16(fp8x8_to_bf16x8(w1[h], w1[h + 1]), qv[i], st1);
+      } else {
+        st0 = mfma_bf16(kr[0][i], qv[i], st0);
+        st1 = mfma_bf16(kr[1][i], qv[i], st1);
+      }
     }
-    // keep the refill below the MFMAs that read kr: hoisting it would need a
-    // second set of K registers
+    // keep the refill below the MFMAs that read the K registers: hoisting it
+    // would need a second set of them
     __builtin_amdgcn_sched_barrier(0);
     load_k(cn);
 
@@ -302,22 +308,33 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     // may hold anything; zero their V so that a zero probability never meets a
     // non-finite value.
     if constexpr (kFp8) {
+      // byte mask over the 8 tokens (code 0 is +0)
+      uint32_t m8[2];
 #pragma unroll
-      for (int i = 0; i < 12; ++i) vr[i] = fp8x8_to_bf16x8(vq[i].x, vq[i].y);
-    }
-    if (__any(okmask != 0xffu)) {
-      u32x4 vm;
+      for (int w = 0; w < 2; ++w) {
+        uint32_t m = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo16 = (okmask >> (2 * w)) & 1u ? 0x0000ffffu : 0u;
-        const uint32_t hi16 = (okmask >> (2 * w + 1)) & 1u ? 0xffff0000u : 0u;
-        vm[w] = lo16 | hi16;
+        for (int k = 0; k < 4; ++k) m |= (okmask >> (4 * w + k)) & 1u ? 0xffu << (8 * k) : 0u;
+        m8[w] = m;
       }
 #pragma unroll
-      for (int i = 0; i < 12; ++i) vr[i] &= vm;
-    }
+      for (int i = 0; i < 12; ++i)
+        acc[i] = mfma_bf16(fp8x8_to_bf16x8(vq[i].x & m8[0], vq[i].y & m8[1]), pb, acc[i]);
+    } else {
+      if (__any(okmask != 0xffu)) {
+        u32x4 vm;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) acc[i] = mfma_bf16(vr[i], pb, acc[i]);
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo16 = (okmask >> (2 * w)) & 1u ? 0x0000ffffu : 0u;
+          const uint32_t hi16 = (okmask >> (2 * w + 1)) & 1u ? 0xffff0000u : 0u;
+          vm[w] = lo16 | hi16;
+        }
+#pragma unroll
+        for (int i = 0; i < 12; ++i) vr[i] &= vm;
+      }
+#pragma unroll
+      for (int i = 0; i < 12; ++i) acc[i] = mfma_bf16(vr[i], pb, acc[i]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_v(cn);
     if (c == c_last) break;

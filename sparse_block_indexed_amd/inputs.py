@@ -22,6 +22,14 @@ Cache layouts (all bf16, all contiguous; the pages fix none of them):
 
 Every (page, group, block) unit of K or V is 3072 contiguous bytes, so the
 unit that block selection picks is also the unit of every HBM read.
+
+One-byte (OCP FP8 E4M3) forms, 1536-byte units with the same addressing:
+
+* K ``[num_pages][4][8 blocks][3 dim-blocks][8 tokens][64 dims]`` -- dim d of a
+  token sits in dim-block d // 64 at d % 64, so the 4 tokens x 64 dims that one
+  load step of the attention kernel reads are 256 contiguous bytes.
+* V ``[num_pages][4][8 blocks][192 dims][8 tokens]``, as in bf16.
+* index keys ``[num_pages][8 blocks][256]``.
 """
 from __future__ import annotations
 
@@ -223,14 +231,16 @@ def quantize_kv_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float
     """One-byte (OCP E4M3) copies of bf16 K/V caches: code = round(x / scale).
 
     K goes from the bf16 layout [page][group][block][24 chunks][8 tokens][8 dims]
-    to the one-byte layout [page][group][block][8 tokens][192 dims]; V keeps its
-    [192 dims][8 tokens] order. Returns uint8 tensors [num_pages][4][8][1536]."""
+    to the one-byte layout [page][group][block][3 dim-blocks][8 tokens][64 dims];
+    V keeps its [192 dims][8 tokens] order. Returns uint8 tensors
+    [num_pages][4][8][1536]."""
     P = k_cache.shape[0]
     kq = torch.empty((P, G, BPP, FP8_UNIT), dtype=torch.uint8, device=k_cache.device)
     vq = torch.empty_like(kq)
     for p0 in range(0, P, chunk_pages):
         p1 = min(P, p0 + chunk_pages)
-        k = k_cache[p0:p1].view(p1 - p0, G, BPP, D // 8, BS, 8).permute(0, 1, 2, 4, 3, 5)
+        # chunk c = 8 * j + c' of the bf16 form -> dim-block j, dims 8c' .. 8c'+7 of it
+        k = k_cache[p0:p1].view(p1 - p0, G, BPP, 3, 8, BS, 8).permute(0, 1, 2, 3, 5, 4, 6)
         k = k.reshape(p1 - p0, G, BPP, FP8_UNIT).float() / k_scale
         kq[p0:p1] = k.to(torch.float8_e4m3fn).view(torch.uint8)
         v = v_cache[p0:p1].float() / v_scale
@@ -241,11 +251,13 @@ def quantize_kv_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float
 def pack_k_rows_fp8(k_codes: torch.Tensor, page_row: np.ndarray, positions, g: int, rows: torch.Tensor) -> None:
     """Store one-byte K rows (uint8 codes, 192 each) in the one-byte K layout."""
     flat = k_codes.view(-1)
+    d = torch.arange(D)
+    dim_off = (d // 64) * (BS * 64) + d % 64
     for i, pos in enumerate(positions):
         page = int(page_row[pos // PS])
         r = pos % PS
-        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT + (r % BS) * D
-        flat[base:base + D] = rows[i].to(flat.device)
+        base = ((page * G + g) * BPP + r // BS) * FP8_UNIT + (r % BS) * 64
+        flat[(base + dim_off).to(flat.device)] = rows[i].to(flat.device)
 
 
 def pack_v_rows_fp8(v_codes: torch.Tensor, page_row: np.ndarray, positions, g: int, rows: torch.Tensor) -> None:

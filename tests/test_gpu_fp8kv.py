@@ -44,7 +44,7 @@ def _dequantize_to_bf16(kv):
     kc, vc, ks, vs = kv
     P = kc.shape[0]
     k = kc.view(torch.float8_e4m3fn).float() * ks
-    k = k.view(P, 4, 8, 8, 24, 8).permute(0, 1, 2, 4, 3, 5).reshape(P, 4, 8, 1536)
+    k = k.view(P, 4, 8, 3, 8, 8, 8).permute(0, 1, 2, 3, 5, 4, 6).reshape(P, 4, 8, 1536)
     v = vc.view(torch.float8_e4m3fn).float() * vs
     return k.to(torch.bfloat16).contiguous(), v.to(torch.bfloat16).contiguous()
 

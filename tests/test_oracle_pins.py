@@ -388,7 +388,7 @@ def test_fp8_kv_layout_hand_offsets_and_packer():
     page_row = np.array([2, 0, 1])
     # hand offsets: K (page 1, group 3, position 70 -> logical page 1 = physical 0, block 0, token 6, dim 100)
     kf = k.view(-1).numpy()
-    kf[((0 * 4 + 3) * 8 + 0) * 1536 + 6 * 192 + 100] = 0x38            # 1.0
+    kf[((0 * 4 + 3) * 8 + 0) * 1536 + 1 * 512 + 6 * 64 + 36] = 0x38    # 1.0 (dim-block 1, dim 64 + 36)
     vf = v.view(-1).numpy()
     vf[((0 * 4 + 3) * 8 + 0) * 1536 + 100 * 8 + 6] = 0xC0              # -2.0
     kr = O.k_rows_fp8(kf, page_row, [70], 3, 0.5)
