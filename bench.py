@@ -13,10 +13,15 @@ batch 1; 2: sliding-window decode at 16K-32K, batch 64; 3: decode at 1M,
 batch 4; 4: a 16,384-token prefill chunk after 112K tokens); the default is
 the headline workload 1.
 
-Prints one JSON line. `value` is query tokens per second of the whole step.
-The roofline object covers the dominant kernel (the attention kernel): its
-algorithmic bytes (distinct K/V blocks read + Q + O + selection + lse) divided by
-its mean duration measured with HIP events on the launch stream.
+The step is captured as HIP graphs and replayed, 10 steps per replay as a
+served forward replays its layers (`--eager` issues every call from Python
+instead); each step runs every kernel of the step on the same resident inputs.
+
+Prints one JSON line. `value` is query tokens per second of the whole step
+(wall clock over back-to-back steps). The roofline object covers the dominant
+kernel (the attention kernel): its algorithmic bytes (distinct K/V blocks read
++ Q + O + selection + lse) divided by its mean duration, measured with HIP
+events on the launch stream around graph replays of 5 back-to-back calls.
 """
 from __future__ import annotations
 
@@ -37,6 +42,7 @@ if ROOT not in sys.path:
 METRIC = "sparse-attn decode query-tokens/s at 128K ctx, batch 64; achieved HBM GB/s"
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+GRAPH_STEPS = 10          # steps per graph replay in the timed loop
 SCALE = 1.0 / math.sqrt(192.0)
 PMC_FILE = os.path.join(ROOT, "profiles", "attention_mtp_verify_128k_pmc.json")
 KERNEL_SOURCE = os.path.join(ROOT, "sparse_block_indexed_amd", "csrc", "sa_attention.hip")
@@ -146,6 +152,8 @@ def main():
     ap.add_argument("--fp8-kv", action="store_true",
                     help="attend one-byte (OCP E4M3) K/V caches quantised from the bf16 ones "
                          "(k_scale 1/32, v_scale 1/16)")
+    ap.add_argument("--eager", action="store_true",
+                    help="issue every call from Python instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
     args = ap.parse_args()
@@ -197,35 +205,96 @@ def main():
     part_lse = torch.empty((n_tok, S, 64), dtype=torch.float32, device=dev) if S > 1 else None
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        if window is None:
-            ops.indexer_topk(wl.q_idx, kidx, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+    def run_indexer():
+        ops.indexer_topk(wl.q_idx, kidx, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
+
+    def run_attention():
         if window is None:
             ops.sparse_decode(wl.q, kc, vc, pt, sl, qs, qp, sel, SCALE, num_splits=S, out=out,
                               out_lse=lse, part_o=part_o, part_lse=part_lse, **kv_kw)
         else:
             ops.swa_decode(wl.q, kc, vc, pt, sl, qs, qp, window, SCALE, num_splits=S, out=out,
                            out_lse=lse, part_o=part_o, part_lse=part_lse, **kv_kw)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def run_step():
+        if window is None:
+            run_indexer()
+        run_attention()
 
     for _ in range(args.warmup):
-        step()
+        run_step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    if args.eager:
+        # every call issued from Python: small steps include the host's launch time
+        launch_step = run_step
+        phases = {"indexer_topk": run_indexer, "attention": run_attention}
+    else:
+        # The step and each phase are captured once as HIP graphs and replayed:
+        # every replay runs all kernels of the step on the same inputs; only the
+        # host's per-call argument handling is gone.
+        def capture(fn, reps=1):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn()
+            torch.cuda.synchronize()
+            return g
+
+        # a served decode forward replays many layers from one graph; GRAPH_STEPS
+        # steps per replay keep the graph launch's fixed host cost out of the
+        # per-step figure in the same way
+        g_one = capture(run_step)
+        g_many = capture(run_step, GRAPH_STEPS)
+        launch_step = g_one.replay
+        phases = {"indexer_topk": run_indexer, "attention": run_attention}
+    if window is not None:
+        del phases["indexer_topk"]
+
+    # exactly args.steps whole steps, back to back: the throughput figure
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    if args.eager:
+        for i in range(args.steps):
+            launch_step()
+    else:
+        for i in range(args.steps // GRAPH_STEPS):
+            g_many.replay()
+        for i in range(args.steps % GRAPH_STEPS):
+            g_one.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+
+    # per-phase duration with HIP events on the launch stream: REPS back-to-back
+    # launches of one phase per timed interval (one graph replay, or REPS eager
+    # calls), so the interval holds that phase's kernels only
+    REPS = 5
+    phase_ms = {}
+    for name, fn in phases.items():
+        runner = (lambda f=fn: [f() for _ in range(REPS)]) if args.eager else capture(fn, REPS).replay
+        runner()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(2, args.steps // REPS)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            runner()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) / REPS)
+        phase_ms[name] = float(np.mean(times))
+    idx_ms = phase_ms.get("indexer_topk", 0.0)
+    attn_ms = phase_ms["attention"]
+    # leave the step's own results in sel / out for the byte counts below
+    run_step()
+    torch.cuda.synchronize()
 
     # cold-cache steps: a 1 GiB write between steps evicts L2 and the 256 MB MALL
     cold_ms = None
@@ -234,12 +303,13 @@ def main():
         cold = []
         for _ in range(args.cold_steps):
             flush.fill_(1.0)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(ev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch_step()
+            e1.record(stream)
             torch.cuda.synchronize()
-            cold.append((ev[0].elapsed_time(ev[2]), ev[1].elapsed_time(ev[2])))
-        cold_ms = float(np.mean([c[0] for c in cold]))
-        cold_attn_ms = float(np.mean([c[1] for c in cold]))
+            cold.append(e0.elapsed_time(e1))
+        cold_ms = float(np.mean(cold))
         del flush
 
     sel_host = sel.cpu().numpy() if window is None else None
@@ -260,6 +330,7 @@ def main():
                           if wl.spec.seq_len_range else str(sorted(set(int(x) for x in wl.seq_lens)))),
               "block_tokens": 8, "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S}
     config["kv_cache"] = "fp8_e4m3" if args.fp8_kv else "bf16"
+    config["launch"] = "eager" if args.eager else "hip_graph"
     if window is None:
         config["topk_blocks"] = topk
         config["index_keys"] = "fp8_e4m3" if args.fp8_index_keys else "bf16"
@@ -283,14 +354,15 @@ def main():
         "data": "synthetic",
         "config": config,
         "achieved_hbm_gbps": (attn_bytes + idx_bytes) / (ms_per_step * 1e-3) / 1e9,
-        "step_breakdown_ms": {"indexer_topk": idx_ms,
-                              ("swa_decode" if window else "sparse_decode"): attn_ms},
+        "step_breakdown_ms": ({} if window else {"indexer_topk": idx_ms}) |
+                             {("swa_decode" if window else "sparse_decode"): attn_ms},
         "algorithmic_bytes": {"indexer_topk": idx_bytes, ("swa_decode" if window else "sparse_decode"): attn_bytes},
         "algorithmic_flops": {"indexer_topk": idx_flops, ("swa_decode" if window else "sparse_decode"): attn_flops},
     }
-    kname = "attention_kernel<%s, %s> (%s%s)" % ("true" if window else "false", "fp8" if args.fp8_kv else "bf16",
-                                                 "sa_swa_decode" if window else "sa_sparse_decode",
-                                                 "_fp8kv" if args.fp8_kv else "")
+    kname = "attention_kernel<%s, %s>%s (%s%s)" % ("true" if window else "false", "fp8" if args.fp8_kv else "bf16",
+                                                   " + merge_kernel" if S > 1 else "",
+                                                   "sa_swa_decode" if window else "sa_sparse_decode",
+                                                   "_fp8kv" if args.fp8_kv else "")
     if W == 4:
         # the prefill chunk is a dense-contraction workload on paper: report MFMA utilisation
         tf = (attn_flops + idx_flops) / (ms_per_step * 1e-3) / 1e12
@@ -311,8 +383,7 @@ def main():
                               "traffic": counter_traffic() if (W == 1 and not args.fp8_kv) else None,
                               "kernel": kname}
     if cold_ms is not None:
-        result["cold_cache"] = {"ms_per_step": cold_ms, "attention_ms": cold_attn_ms,
-                                "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}
+        result["cold_cache"] = {"ms_per_step": cold_ms, "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, sel_host, window,
                                               kv_fp8=(kc, vc, kv_kw["k_scale"], kv_kw["v_scale"])

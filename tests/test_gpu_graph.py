@@ -1,0 +1,134 @@
+"""The library's calls under HIP graph capture: a captured step replayed several
+times, with eager work and synchronisations between the replays, must give
+bitwise the results of the same calls run eagerly (every kernel is
+deterministic and the inputs do not change). The library enqueues kernels
+only: no allocation, no memset, no synchronisation inside a call.
+"""
+import math
+
+import pytest
+import torch
+
+from sparse_block_indexed_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(192.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_block_indexed_amd import ops
+    ops.load_library()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+class _Step:
+    """Preallocated buffers and the calls of one step (sparse layer + window layer)."""
+
+    def __init__(self, wl, num_splits, fp8_kv=False):
+        from sparse_block_indexed_amd import ops
+        self.ops = ops
+        self.wl = wl
+        dev = wl.q.device
+        self.tabs = wl.device_ints(dev)
+        n = wl.n_tok
+        if fp8_kv:
+            kc, vc = I.quantize_kv_fp8(wl.k_cache, wl.v_cache, 1 / 32, 1 / 16)
+            self.kv = (kc, vc, dict(k_scale=1 / 32, v_scale=1 / 16))
+        else:
+            self.kv = (wl.k_cache, wl.v_cache, {})
+        self.S = ops.resolve_num_splits(n, 513, num_splits)
+        self.Sw = ops.resolve_num_splits(n, 512 // 8 + 2, num_splits)
+        self.num_splits = num_splits
+        self.sel = torch.empty((n, 512), dtype=torch.int32, device=dev)
+        self.ws = torch.empty(ops.indexer_workspace_size(n, wl.max_pages_per_seq, 512), dtype=torch.uint8,
+                              device=dev)
+        mk = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+        self.out = torch.empty((n, 64, 192), dtype=torch.bfloat16, device=dev)
+        self.lse = mk(n, 64)
+        self.po = mk(n, self.S, 64, 192) if self.S > 1 else None
+        self.pl = mk(n, self.S, 64) if self.S > 1 else None
+        self.wout = torch.empty_like(self.out)
+        self.wlse = mk(n, 64)
+        self.wpo = mk(n, self.Sw, 64, 192) if self.Sw > 1 else None
+        self.wpl = mk(n, self.Sw, 64) if self.Sw > 1 else None
+
+    def run(self):
+        ops, wl = self.ops, self.wl
+        pt, sl, qs, qp = self.tabs
+        kc, vc, kw = self.kv
+        ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, 512, sel_idx=self.sel, workspace=self.ws)
+        ops.sparse_decode(wl.q, kc, vc, pt, sl, qs, qp, self.sel, SCALE, num_splits=self.num_splits, out=self.out,
+                          out_lse=self.lse, part_o=self.po, part_lse=self.pl, **kw)
+        ops.swa_decode(wl.q, kc, vc, pt, sl, qs, qp, 512, SCALE, num_splits=self.num_splits, out=self.wout,
+                       out_lse=self.wlse, part_o=self.wpo, part_lse=self.wpl, **kw)
+
+    def outputs(self):
+        return [self.sel, self.out, self.lse, self.wout, self.wlse]
+
+    def poison(self):
+        self.sel.fill_(-7)
+        for t in (self.out, self.lse, self.wout, self.wlse):
+            t.fill_(float("nan"))
+
+
+def _graph_vs_eager(wl, num_splits, fp8_kv=False, replays=3):
+    step = _Step(wl, num_splits, fp8_kv)
+    step.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in step.outputs()]
+    # warm up on a side stream, then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    torch.cuda.synchronize()
+    other = _Step(wl, num_splits, fp8_kv)
+    for r in range(replays):
+        step.poison()
+        other.run()                       # eager work of the program between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(["sel", "out", "lse", "swa out", "swa lse"], step.outputs(), ref):
+            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager result"
+    for got, want in zip(other.outputs(), ref):
+        assert torch.equal(got, want)
+
+
+SMALL = I.WorkloadSpec("small_mixed", batch=12,
+                       seq_lens=[1, 7, 8, 9, 63, 64, 65, 300, 1000, 4103, 4111, 9000],
+                       q_per_seq=3, spare_pages=5)
+
+
+@pytest.mark.parametrize("num_splits,fp8_kv", [(1, False), (3, False), (0, True)])
+def test_small_step_graph_replays_match_eager(num_splits, fp8_kv):
+    _say(f"graph small S={num_splits} fp8_kv={fp8_kv}")
+    wl = I.make_workload(SMALL, seed=71, device="cuda")
+    _graph_vs_eager(wl, num_splits, fp8_kv)
+
+
+def test_long_history_step_graph_replays_match_eager():
+    """Histories past the fused-select limit (zero + collect launches) under capture."""
+    _say("graph long history")
+    wl = I.make_workload(I.WorkloadSpec("long", batch=2, seq_lens=[200000, 30000], q_per_seq=2), seed=72,
+                         device="cuda")
+    _graph_vs_eager(wl, 0)
+
+
+def test_config1_step_graph_replays_match_eager():
+    """The 128K MTP verify workload as the benchmark replays it."""
+    _say("graph config 1")
+    wl = I.config_workload(1, device="cuda")
+    _graph_vs_eager(wl, 0, replays=2)
