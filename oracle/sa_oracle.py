@@ -30,7 +30,10 @@ Readings where the pages are silent (each is listed in the design notes):
   "Fitting it on a node": FP8 KV for the full-attention layers, lossy): value =
   E4M3 code * per-cache scale; attention is the same exact softmax over the
   decoded values.
-* One selection per query token, shared by all four KV groups.
+* One selection per query token, shared by all four KV groups (the default);
+  or, the other reading of "each KV group picks" in the open-weights blog's
+  "What sparse attention does and doesn't save", one index query and one top-k
+  set per (token, KV group) over the same one-per-block keys.
 * Historical blocks of a token at position p are blocks 0 .. floor(p/8)-1; the
   current block floor(p/8) is always attended, its tokens up to p only.
 * "Up to 512": if fewer historical blocks exist, all are kept.
@@ -279,6 +282,47 @@ def merge(part_o: np.ndarray, part_lse: np.ndarray):
 # ---------------------------------------------------------------------------
 # Whole-token drivers over a paged workload (host copies of the caches)
 # ---------------------------------------------------------------------------
+
+def attend_positions_by_group(q_heads, k_cache_bits, v_cache_bits, page_row, positions_by_group, scale,
+                              fp8_scales=None):
+    """Attention of one token where KV group g attends its own token positions
+    positions_by_group[g] (the heads of group g see only those)."""
+    ks, vs = [], []
+    for g in range(G):
+        pos = positions_by_group[g]
+        if fp8_scales is None:
+            ks.append(k_rows(k_cache_bits, page_row, pos, g))
+            vs.append(v_rows(v_cache_bits, page_row, pos, g))
+        else:
+            ks.append(k_rows_fp8(k_cache_bits, page_row, pos, g, fp8_scales[0]))
+            vs.append(v_rows_fp8(v_cache_bits, page_row, pos, g, fp8_scales[1]))
+    return attend(q_heads, ks, vs, scale)
+
+
+# Per-KV-group selection (open-weights blog, "What sparse attention does and
+# doesn't save": each KV group picks its own up-to-512 historical blocks plus
+# the current one). The index key stays one per block; each group brings its
+# own index query, scores the same keys and keeps its own top-k.
+
+def sparse_layer_token_grouped(q_heads_bits, q_idx_bits_by_group, k_cache_bits, v_cache_bits, kidx_bits,
+                               page_row, p: int, k: int, scale: float, fp8_scales=None, kidx_fp8=False):
+    """Per-group indexer -> top-k -> attention, for one query token.
+    q_idx_bits_by_group: [4][256] bf16 bits. Returns (sel [4][k], O [64][192], lse [64])."""
+    cb = current_block(p)
+    keys = index_keys(kidx_bits, page_row, cb, fp8=kidx_fp8)
+    sels = np.stack([indexer_topk_token(bf16_to_f64(q_idx_bits_by_group[g]), keys, k) for g in range(G)])
+    O, lse = sparse_attention_token_grouped(q_heads_bits, k_cache_bits, v_cache_bits, page_row, sels, p, scale,
+                                            fp8_scales)
+    return sels, O, lse
+
+
+def sparse_attention_token_grouped(q_heads_bits, k_cache_bits, v_cache_bits, page_row, sels, p, scale,
+                                   fp8_scales=None):
+    """Attention of one query token given each group's selected blocks (sels [4][k])."""
+    pos = [sparse_token_positions(np.asarray(sels[g]), p) for g in range(G)]
+    return attend_positions_by_group(bf16_to_f64(q_heads_bits), k_cache_bits, v_cache_bits, page_row, pos,
+                                     scale, fp8_scales)
+
 
 def sparse_layer_token(q_heads_bits, q_idx_bits, k_cache_bits, v_cache_bits, kidx_bits,
                        page_row, p: int, k: int, scale: float):

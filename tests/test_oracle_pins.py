@@ -436,3 +436,72 @@ def test_fp8_kv_attention_equals_sdpa_on_decoded_rows(seq_len):
     dv8 = (dv.float() / vs).to(torch.float8_e4m3fn).double() * vs
     ref = _sdpa(q, dk8, dv8, list(range(p + 1)))
     np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# Per-KV-group selection
+# ---------------------------------------------------------------------------
+
+def _grouped_inputs(seq_len, seed):
+    page_row, dk, dv, q, kc, vc = _dense_seq(seq_len, seed=seed)
+    g = torch.Generator().manual_seed(seed + 100)
+    kidx = torch.randint(-4, 5, (kc.shape[0], 8, 256), generator=g).to(torch.bfloat16)
+    qg = torch.randint(-4, 5, (4, 256), generator=g).to(torch.bfloat16)
+    return page_row, dk, dv, q, kc, vc, kidx, qg
+
+
+def test_grouped_selection_with_equal_queries_is_the_shared_selection():
+    page_row, dk, dv, q, kc, vc, kidx, qg = _grouped_inputs(5000, seed=81)
+    qg[:] = qg[0]
+    p = 4999
+    args = (I.bf16_bits(kc), I.bf16_bits(vc), I.bf16_bits(kidx), page_row, p, 512, SCALE)
+    sels, out_g, lse_g = O.sparse_layer_token_grouped(I.bf16_bits(q), I.bf16_bits(qg), *args)
+    sel, out, lse = O.sparse_layer_token(I.bf16_bits(q), I.bf16_bits(qg[0]), *args)
+    for g in range(4):
+        assert sels[g].tolist() == sel.tolist()
+    np.testing.assert_array_equal(out_g, out)
+    np.testing.assert_array_equal(lse_g, lse)
+
+
+@pytest.mark.parametrize("seq_len", [9, 700, 5000])
+def test_grouped_heads_of_each_group_match_the_shared_layer_with_that_query(seq_len):
+    """Group g's 16 heads see exactly what the shared layer gives them when the
+    whole token uses group g's index query."""
+    page_row, dk, dv, q, kc, vc, kidx, qg = _grouped_inputs(seq_len, seed=82 + seq_len)
+    p = seq_len - 1
+    args = (I.bf16_bits(kc), I.bf16_bits(vc), I.bf16_bits(kidx), page_row, p, 512, SCALE)
+    sels, out_g, lse_g = O.sparse_layer_token_grouped(I.bf16_bits(q), I.bf16_bits(qg), *args)
+    distinct = set()
+    for g in range(4):
+        sel, out, lse = O.sparse_layer_token(I.bf16_bits(q), I.bf16_bits(qg[g]), *args)
+        assert sels[g].tolist() == sel.tolist()
+        h = slice(16 * g, 16 * g + 16)
+        np.testing.assert_array_equal(out_g[h], out[h])
+        np.testing.assert_array_equal(lse_g[h], lse[h])
+        distinct.add(tuple(sel.tolist()))
+    if p // 8 > 512:
+        assert len(distinct) > 1          # the groups really chose differently
+
+
+def test_grouped_layer_against_brute_force_and_sdpa():
+    """Per group: top-k by brute-force integer scores (Python loops, ties to the
+    lower block), then torch SDPA over that group's tokens for its 16 heads."""
+    seq_len, k = 64 * 4 + 13, 6
+    page_row, dk, dv, q, kc, vc, kidx, qg = _grouped_inputs(seq_len, seed=90)
+    p = seq_len - 1
+    cb = p // 8
+    sels, out_g, lse_g = O.sparse_layer_token_grouped(I.bf16_bits(q), I.bf16_bits(qg), I.bf16_bits(kc),
+                                                      I.bf16_bits(vc), I.bf16_bits(kidx), page_row, p, k, SCALE)
+    kid = kidx.to(torch.int64)
+    for g in range(4):
+        qi = [int(x) for x in qg[g].to(torch.int64)]
+        scores = []
+        for blk in range(cb):
+            row = kid[int(page_row[blk // 8]), blk % 8]
+            scores.append(sum(qi[d] * int(row[d]) for d in range(256)))
+        order = sorted(range(cb), key=lambda b: (-scores[b], b))[:k]
+        assert sels[g].tolist() == sorted(order)
+        positions = [8 * b + i for b in sorted(order) for i in range(8)] + list(range(8 * cb, p + 1))
+        ref = _sdpa(q, dk, dv, positions)
+        h = slice(16 * g, 16 * g + 16)
+        np.testing.assert_allclose(out_g[h], ref[h], atol=1e-12, rtol=0)
