@@ -66,10 +66,13 @@ def counter_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: int = 64, kv_fp8=None):
+def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: int = 64, kv_fp8=None,
+                 q_groups=None, kidx_fp8=None):
     """The fp64 oracle timed on this host over a bounded sample of the same
     workload: whole sequences' query tokens, until the budget is spent.
-    kv_fp8 = (k_codes, v_codes, k_scale, v_scale) times the one-byte form."""
+    kv_fp8 = (k_codes, v_codes, k_scale, v_scale) times the one-byte KV form,
+    kidx_fp8 (E4M3 codes) the one-byte index keys, q_groups ([n_tok][4][256]
+    index queries) per-KV-group selection."""
     import torch
     from oracle import sa_oracle as O
     from sparse_block_indexed_amd import inputs as I
@@ -92,12 +95,14 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
         npg = (max_cb + 7) // 8
         kidx = None
         if window is None:
-            kidx = I.bf16_bits(wl.k_idx_cache.index_select(0, torch.as_tensor(row[:npg].astype(np.int64), device=dev)))
+            prow = torch.as_tensor(row[:npg].astype(np.int64), device=dev)
+            kidx = (I.bf16_bits(wl.k_idx_cache.index_select(0, prow)) if kidx_fp8 is None
+                    else kidx_fp8.index_select(0, prow).cpu().numpy())
         pages = set()
         for t in toks:
             p = int(wl.q_pos[t])
             if window is None:
-                pages |= {int(x) // 8 for x in sel_host[t] if x >= 0} | {p // 64}
+                pages |= {int(x) // 8 for x in np.asarray(sel_host[t]).reshape(-1) if x >= 0} | {p // 64}
             else:
                 pages |= set(range(max(0, p - window + 1) // 64, p // 64 + 1))
         logical = np.array(sorted(pages), dtype=np.int64)
@@ -111,17 +116,22 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
         compact = np.full(row.shape[0], -1, dtype=np.int64)
         compact[logical] = np.arange(len(logical))
         qb = [I.bf16_bits(wl.q[t]) for t in toks]
-        qib = [I.bf16_bits(wl.q_idx[t]) for t in toks]
+        qib = [I.bf16_bits(wl.q_idx[t] if q_groups is None else q_groups[t]) for t in toks]
         t0 = time.perf_counter()
         for j, t in enumerate(toks):
             p = int(wl.q_pos[t])
-            if window is None:
-                keys = O.index_keys(kidx, np.arange(npg), p // 8)
+            if window is not None:
+                O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.window_positions(p, window), SCALE,
+                                   fp8_scales=fp8_scales)
+            elif q_groups is None:
+                keys = O.index_keys(kidx, np.arange(npg), p // 8, fp8=kidx_fp8 is not None)
                 sel = O.indexer_topk_token(O.bf16_to_f64(qib[j]), keys, 512)
-                pos = O.sparse_token_positions(sel, p)
+                O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.sparse_token_positions(sel, p), SCALE,
+                                   fp8_scales=fp8_scales)
             else:
-                pos = O.window_positions(p, window)
-            O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, pos, SCALE, fp8_scales=fp8_scales)
+                keys = O.index_keys(kidx, np.arange(npg), p // 8, fp8=kidx_fp8 is not None)
+                sels = [O.indexer_topk_token(O.bf16_to_f64(qib[j][g]), keys, 512) for g in range(4)]
+                O.sparse_attention_token_grouped(qb[j], kc, vc, compact, sels, p, SCALE, fp8_scales=fp8_scales)
             done += 1
             if time.perf_counter() - t0 + t_cpu >= budget_s:
                 break
@@ -152,6 +162,8 @@ def main():
     ap.add_argument("--fp8-kv", action="store_true",
                     help="attend one-byte (OCP E4M3) K/V caches quantised from the bf16 ones "
                          "(k_scale 1/32, v_scale 1/16)")
+    ap.add_argument("--per-group-selection", action="store_true",
+                    help="one index query and one top-512 set per (token, KV group) instead of per token")
     ap.add_argument("--eager", action="store_true",
                     help="issue every call from Python instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +197,8 @@ def main():
     wl = I.config_workload(W, device=dev)
     pt, sl, qs, qp = wl.device_ints(dev)
     kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if args.fp8_index_keys else wl.k_idx_cache
+    per_group = args.per_group_selection
+    qidx = I.grouped_index_queries(wl.n_tok, seed=1000 + W, device=dev) if per_group else wl.q_idx
     if args.fp8_kv:
         k_scale, v_scale = 1.0 / 32, 1.0 / 16
         kc, vc = I.quantize_kv_fp8(wl.k_cache, wl.v_cache, k_scale, v_scale)
@@ -196,8 +210,8 @@ def main():
     n_tok = wl.n_tok
     max_blocks = (window // 8 + 2) if window else topk + 1
     S = ops.resolve_num_splits(n_tok, max_blocks, args.num_splits)
-    sel = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
-    ws = None if window else torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk),
+    sel = torch.empty((n_tok, 4, topk) if per_group else (n_tok, topk), dtype=torch.int32, device=dev)
+    ws = None if window else torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk, per_group),
                                          dtype=torch.uint8, device=dev)
     out = torch.empty((n_tok, 64, 192), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((n_tok, 64), dtype=torch.float32, device=dev)
@@ -206,7 +220,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def run_indexer():
-        ops.indexer_topk(wl.q_idx, kidx, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
+        ops.indexer_topk(qidx, kidx, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
 
     def run_attention():
         if window is None:
@@ -314,7 +328,13 @@ def main():
 
     sel_host = sel.cpu().numpy() if window is None else None
     kvb = 1 if args.fp8_kv else 2
-    if window is None:
+    if window is None and per_group:
+        attn_bytes = B.sparse_attention_bytes_grouped(wl.q_seq, wl.q_pos, sel_host, kv_bytes=kvb)
+        idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk, key_bytes=1 if args.fp8_index_keys else 2,
+                                         queries_per_token=4)
+        attn_flops = sum(B.sparse_attention_flops(wl.q_pos, sel_host[:, g], num_heads=16) for g in range(4))
+        idx_flops = 4 * B.indexer_flops(wl.q_pos)
+    elif window is None:
         attn_bytes = B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host, kv_bytes=kvb)
         idx_bytes = B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk, key_bytes=1 if args.fp8_index_keys else 2)
         attn_flops = B.sparse_attention_flops(wl.q_pos, sel_host)
@@ -334,9 +354,11 @@ def main():
     if window is None:
         config["topk_blocks"] = topk
         config["index_keys"] = "fp8_e4m3" if args.fp8_index_keys else "bf16"
+        config["selection"] = "per_kv_group" if per_group else "per_token"
     else:
         config["window"] = window
-    tags = [t for t, on in (("fp8 index keys", args.fp8_index_keys), ("fp8 KV", args.fp8_kv)) if on]
+    tags = [t for t, on in (("fp8 index keys", args.fp8_index_keys), ("fp8 KV", args.fp8_kv),
+                            ("per-KV-group selection", per_group)) if on]
     metric = METRIC if (W == 1 and not tags) else \
         f"{names[W]}{' (' + ', '.join(tags) + ')' if tags else ''} query-tokens/s; achieved HBM GB/s"
     result = {
@@ -387,7 +409,9 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, sel_host, window,
                                               kv_fp8=(kc, vc, kv_kw["k_scale"], kv_kw["v_scale"])
-                                              if args.fp8_kv else None)
+                                              if args.fp8_kv else None,
+                                              q_groups=qidx if per_group else None,
+                                              kidx_fp8=kidx if args.fp8_index_keys else None)
     print(json.dumps(result), flush=True)
 
 

@@ -64,6 +64,10 @@ extern "C" {
 #define SA_MAX_WINDOW 4096
 #define SA_MAX_SPLITS 64
 
+/* Storage formats of a cache (index keys or K/V) for the entry points that take one. */
+#define SA_FORMAT_BF16 0
+#define SA_FORMAT_FP8_E4M3 1
+
 typedef enum {
   SA_OK = 0,
   SA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment */
@@ -134,6 +138,29 @@ sa_status sa_indexer_topk_fp8(const void* q_idx, const void* k_idx_cache_fp8, sa
                               const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
                               int32_t* sel_idx, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Per-KV-group selection. (Open-weights blog, "What sparse attention does and
+ * doesn't save": each KV group picks its own historical blocks.) The index key
+ * stays one per block; each of a token's 4 KV groups brings its own index query
+ * and keeps its own top-k blocks, scored and chosen exactly as in
+ * sa_indexer_topk.
+ *
+ * q_idx        device bf16 [n_tok][4][256] (query of token t, group g at [t][g])
+ * k_idx_cache  device [num_pages][8][256], bf16 (key_format SA_FORMAT_BF16) or
+ *              OCP E4M3 codes (SA_FORMAT_FP8_E4M3, as for sa_indexer_topk_fp8)
+ * sel_idx      device int32 [n_tok][4][topk], out: per (token, group) ascending
+ *              block ids, -1 padded
+ * workspace    at least sa_indexer_topk_grouped_workspace_size() bytes
+ * Other arguments as for sa_indexer_topk. Another key_format gives
+ * SA_ERR_UNSUPPORTED, as does n_tok >= 2^29.
+ */
+size_t sa_indexer_topk_grouped_workspace_size(int n_tok, int max_pages_per_seq, int topk);
+
+sa_status sa_indexer_topk_grouped(const void* q_idx, const void* k_idx_cache, int key_format,
+                                  sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
+                                  int n_tok, int topk, int32_t* sel_idx, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /* Number of partitions a decode call uses for a given request
  * (num_splits > 0 is returned clamped to SA_MAX_SPLITS; 0 picks from n_tok and
  * max_blocks_per_token so that the grid fills the GPU). */
@@ -164,6 +191,24 @@ sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cac
                            const int32_t* sel_idx, int n_tok, int topk, float softmax_scale,
                            int num_splits, float* part_o, float* part_lse, void* out,
                            float* out_lse, hipStream_t stream);
+
+/*
+ * Block-sparse GQA attention with one selection per KV group (as written by
+ * sa_indexer_topk_grouped): the 16 heads of group g attend the tokens of the
+ * blocks in sel_idx[t][g] and of the current block up to p.
+ *
+ * sel_idx      device int32 [n_tok][4][topk]
+ * kv_format    SA_FORMAT_BF16 (k_scale and v_scale are ignored) or
+ *              SA_FORMAT_FP8_E4M3 (one-byte caches and scales as for
+ *              sa_sparse_decode_fp8kv); another value gives SA_ERR_UNSUPPORTED
+ * Every other argument and every output is as for sa_sparse_decode.
+ */
+sa_status sa_sparse_decode_grouped(const void* q, const void* k_cache, const void* v_cache,
+                                   int kv_format, float k_scale, float v_scale, sa_paged_desc pd,
+                                   const int32_t* q_seq, const int32_t* q_pos,
+                                   const int32_t* sel_idx, int n_tok, int topk, float softmax_scale,
+                                   int num_splits, float* part_o, float* part_lse, void* out,
+                                   float* out_lse, hipStream_t stream);
 
 /*
  * Sliding-window GQA attention: token t at position p attends positions

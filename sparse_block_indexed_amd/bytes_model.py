@@ -49,7 +49,8 @@ def indexer_read_bytes_per_step(context: int, sparse_layers: int = 23, key_bytes
 # Per-launch algorithmic traffic of this library's kernels
 # ---------------------------------------------------------------------------
 
-def indexer_topk_bytes(q_seq: np.ndarray, q_pos: np.ndarray, topk: int, key_bytes: int = BF16) -> int:
+def indexer_topk_bytes(q_seq: np.ndarray, q_pos: np.ndarray, topk: int, key_bytes: int = BF16,
+                       queries_per_token: int = 1) -> int:
     """Each sequence's index keys once (up to its longest history; key_bytes per
     value), the index queries, and the selection written."""
     q_seq = np.asarray(q_seq)
@@ -57,8 +58,8 @@ def indexer_topk_bytes(q_seq: np.ndarray, q_pos: np.ndarray, topk: int, key_byte
     total = 0
     for b in np.unique(q_seq):
         total += int((q_pos[q_seq == b] // BS).max()) * DI * key_bytes
-    total += len(q_seq) * DI * BF16          # index queries
-    total += len(q_seq) * topk * 4           # sel_idx (int32)
+    total += len(q_seq) * queries_per_token * DI * BF16          # index queries
+    total += len(q_seq) * queries_per_token * topk * 4           # sel_idx (int32)
     return total
 
 
@@ -86,6 +87,26 @@ def sparse_attention_bytes(q_seq, q_pos, sel_idx: np.ndarray, num_heads: int = H
     units = unique_kv_units(q_seq, q_pos, blocks)
     total = units * G * 2 * BS * D * kv_bytes
     total += n_tok * num_heads * D * BF16 * 2       # Q in, O out
+    total += sel_idx.size * 4
+    if write_lse:
+        total += n_tok * num_heads * 4
+    return total
+
+
+def sparse_attention_bytes_grouped(q_seq, q_pos, sel_idx: np.ndarray, num_heads: int = H,
+                                   write_lse: bool = True, kv_bytes: int = BF16) -> int:
+    """Per-KV-group selection (sel_idx [n_tok][4][k]): distinct (sequence, group,
+    block) K and V units, Q read, O written, the selections read, lse written."""
+    sel_idx = np.asarray(sel_idx)
+    n_tok = len(q_seq)
+    units = 0
+    for g in range(G):
+        def blocks(t, g=g):
+            s = sel_idx[t, g]
+            return list(s[s >= 0]) + [int(q_pos[t]) // BS]
+        units += unique_kv_units(q_seq, q_pos, blocks)
+    total = units * 2 * BS * D * kv_bytes
+    total += n_tok * num_heads * D * BF16 * 2
     total += sel_idx.size * 4
     if write_lse:
         total += n_tok * num_heads * 4

@@ -12,6 +12,7 @@ namespace {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kMaxPagesPerSeq = 1 << 20;   // positions stay below 2^26
 constexpr int kMaxPoolPages = 1 << 25;     // (page * 4 + group) * 8 + block fits in int32
+constexpr int kMaxGroupedTokens = (1 << 29) - 1;   // tokens x 4 query rows fit in int32
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -33,7 +34,7 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* q_seq, const int32_t* q_pos, int n_tok, float softmax_scale,
                         int max_blocks, int num_splits, float* part_o, float* part_lse, void* out,
                         float* out_lse, bool window_mode, const int32_t* sel_idx, int topk, int window,
-                        bool kv_fp8, float k_scale, float v_scale, hipStream_t stream) {
+                        bool kv_fp8, float k_scale, float v_scale, bool sel_per_group, hipStream_t stream) {
   if (n_tok < 0 || num_splits < 0) return SA_ERR_INVALID_ARG;
   if (n_tok == 0) return SA_OK;
   if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return SA_ERR_INVALID_ARG;
@@ -73,6 +74,7 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   if (!isfinite(a.scale_log2)) return SA_ERR_INVALID_ARG;
   a.kv_fp8 = kv_fp8;
   a.v_scale = v_scale;
+  a.sel_per_group = sel_per_group;
   // Many query tokens per sequence (a prefill chunk) re-read the same blocks:
   // keep them cacheable then; decode-like calls stream them.
   a.stream_kv = n_tok <= 64 * pd.batch;
@@ -123,10 +125,14 @@ int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits) {
 }
 
 static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, bool key_fp8, sa_paged_desc pd,
-                                   const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
-                                   int32_t* sel_idx, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                                   const int32_t* q_seq, const int32_t* q_pos, int n_tok, bool per_group,
+                                   int topk, int32_t* sel_idx, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
   if (n_tok < 0) return SA_ERR_INVALID_ARG;
   if (n_tok == 0) return SA_OK;
+  if (per_group && n_tok > kMaxGroupedTokens) return SA_ERR_UNSUPPORTED;
+  // one query row per token, or one per (token, KV group)
+  const int n_rows = per_group ? n_tok * sa::kGroups : n_tok;
   if (q_idx == nullptr || k_idx_cache == nullptr || sel_idx == nullptr || workspace == nullptr)
     return SA_ERR_INVALID_ARG;
   if (!aligned(q_idx, 16) || !aligned(k_idx_cache, 16) || !aligned(sel_idx, 4) || !aligned(workspace, 256))
@@ -135,7 +141,7 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   if (st != SA_OK) return st;
   if ((st = check_tokens(q_seq, q_pos)) != SA_OK) return st;
   if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
-  const sa::IndexerWorkspace w = sa::indexer_workspace_layout(n_tok, pd.max_pages_per_seq);
+  const sa::IndexerWorkspace w = sa::indexer_workspace_layout(n_rows, pd.max_pages_per_seq);
   if (ws_bytes < w.total) return SA_ERR_WORKSPACE;
 
   sa::IndexerArgs a;
@@ -145,7 +151,8 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   a.seq_lens = pd.seq_lens;
   a.q_seq = q_seq;
   a.q_pos = q_pos;
-  a.n_tok = n_tok;
+  a.n_tok = n_rows;
+  a.q_shift = per_group ? 2 : 0;
   a.topk = topk;
   a.batch = pd.batch;
   a.max_pages = pd.max_pages_per_seq;
@@ -154,8 +161,8 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   // Query tokens of one sequence are scored in one pass over its keys; the
   // group size guesses how many consecutive tokens share a sequence (any guess
   // is correct, a good one reads each key once).
-  a.group_size = std::max(1, std::min(4, n_tok / pd.batch));
-  const int ngroups = (n_tok + a.group_size - 1) / a.group_size;
+  a.group_size = std::max(1, std::min(4, n_rows / pd.batch));
+  const int ngroups = (n_rows + a.group_size - 1) / a.group_size;
   // Few long workgroups: about two per CU (the score kernel's occupancy), so
   // each workgroup's fixed start-up cost is paid about once per CU.
   int chunk = 4096;
@@ -164,7 +171,7 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   a.bitmap_words = a.max_hist_blocks <= sa::kBitmapMaxBlocks ? (a.max_hist_blocks + 31) / 32 : 0;
   // Many query tokens per sequence (a prefill chunk): the score product is a
   // dense GEMM and runs on MFMA; histories must fit the finalize-only select.
-  a.use_gemm = n_tok >= 64 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
+  a.use_gemm = n_rows >= 64 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
   a.key_fp8 = key_fp8;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
@@ -179,15 +186,29 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
 sa_status sa_indexer_topk(const void* q_idx, const void* k_idx_cache, sa_paged_desc pd, const int32_t* q_seq,
                           const int32_t* q_pos, int n_tok, int topk, int32_t* sel_idx, void* workspace,
                           size_t ws_bytes, hipStream_t stream) {
-  return indexer_topk_impl(q_idx, k_idx_cache, false, pd, q_seq, q_pos, n_tok, topk, sel_idx, workspace, ws_bytes,
-                           stream);
+  return indexer_topk_impl(q_idx, k_idx_cache, false, pd, q_seq, q_pos, n_tok, false, topk, sel_idx, workspace,
+                           ws_bytes, stream);
+}
+
+size_t sa_indexer_topk_grouped_workspace_size(int n_tok, int max_pages_per_seq, int topk) {
+  (void)topk;
+  if (n_tok <= 0 || max_pages_per_seq <= 0 || n_tok > kMaxGroupedTokens) return 0;
+  return sa::indexer_workspace_layout(n_tok * sa::kGroups, max_pages_per_seq).total;
+}
+
+sa_status sa_indexer_topk_grouped(const void* q_idx, const void* k_idx_cache, int key_format, sa_paged_desc pd,
+                                  const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
+                                  int32_t* sel_idx, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (key_format != SA_FORMAT_BF16 && key_format != SA_FORMAT_FP8_E4M3) return SA_ERR_UNSUPPORTED;
+  return indexer_topk_impl(q_idx, k_idx_cache, key_format == SA_FORMAT_FP8_E4M3, pd, q_seq, q_pos, n_tok, true,
+                           topk, sel_idx, workspace, ws_bytes, stream);
 }
 
 sa_status sa_indexer_topk_fp8(const void* q_idx, const void* k_idx_cache_fp8, sa_paged_desc pd,
                               const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk, int32_t* sel_idx,
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
-  return indexer_topk_impl(q_idx, k_idx_cache_fp8, true, pd, q_seq, q_pos, n_tok, topk, sel_idx, workspace,
-                           ws_bytes, stream);
+  return indexer_topk_impl(q_idx, k_idx_cache_fp8, true, pd, q_seq, q_pos, n_tok, false, topk, sel_idx,
+                           workspace, ws_bytes, stream);
 }
 
 sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,
@@ -199,7 +220,7 @@ sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cac
     if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
   }
   return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
-                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, false, 1.f, 1.f, stream);
+                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, false, 1.f, 1.f, false, stream);
 }
 
 sa_status sa_sparse_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8, float k_scale,
@@ -211,7 +232,25 @@ sa_status sa_sparse_decode_fp8kv(const void* q, const void* k_cache_fp8, const v
     if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
   }
   return decode_common(q, k_cache_fp8, v_cache_fp8, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
-                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, true, k_scale, v_scale, stream);
+                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, true, k_scale, v_scale, false,
+                       stream);
+}
+
+sa_status sa_sparse_decode_grouped(const void* q, const void* k_cache, const void* v_cache, int kv_format,
+                                   float k_scale, float v_scale, sa_paged_desc pd, const int32_t* q_seq,
+                                   const int32_t* q_pos, const int32_t* sel_idx, int n_tok, int topk,
+                                   float softmax_scale, int num_splits, float* part_o, float* part_lse, void* out,
+                                   float* out_lse, hipStream_t stream) {
+  if (kv_format != SA_FORMAT_BF16 && kv_format != SA_FORMAT_FP8_E4M3) return SA_ERR_UNSUPPORTED;
+  const bool fp8 = kv_format == SA_FORMAT_FP8_E4M3;
+  if (n_tok > 0) {
+    if (sel_idx == nullptr || !aligned(sel_idx, 4)) return SA_ERR_INVALID_ARG;
+    if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
+    if (n_tok > kMaxGroupedTokens) return SA_ERR_UNSUPPORTED;
+  }
+  return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
+                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, fp8, fp8 ? k_scale : 1.f,
+                       fp8 ? v_scale : 1.f, true, stream);
 }
 
 sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,
@@ -220,7 +259,7 @@ sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
                         hipStream_t stream) {
   if (n_tok > 0 && (window < 1 || window > SA_MAX_WINDOW)) return SA_ERR_UNSUPPORTED;
   return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, window / 8 + 2, num_splits,
-                       part_o, part_lse, out, out_lse, true, nullptr, 0, window, false, 1.f, 1.f, stream);
+                       part_o, part_lse, out, out_lse, true, nullptr, 0, window, false, 1.f, 1.f, false, stream);
 }
 
 sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8, float k_scale,
@@ -230,7 +269,7 @@ sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void
   if (n_tok > 0 && (window < 1 || window > SA_MAX_WINDOW)) return SA_ERR_UNSUPPORTED;
   return decode_common(q, k_cache_fp8, v_cache_fp8, pd, q_seq, q_pos, n_tok, softmax_scale, window / 8 + 2,
                        num_splits, part_o, part_lse, out, out_lse, true, nullptr, 0, window, true, k_scale, v_scale,
-                       stream);
+                       false, stream);
 }
 
 sa_status sa_merge(const float* part_o, const float* part_lse, int n_tok, int num_splits, int num_heads,

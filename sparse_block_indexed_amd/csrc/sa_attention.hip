@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     if (kWindow) {
       beta = b_lo + slot;
     } else if (slot < nsel) {
-      beta = a.sel_idx[(size_t)t * a.topk + slot];
+      beta = a.sel_idx[((size_t)t * (a.sel_per_group ? kGroups : 1) + (a.sel_per_group ? g : 0)) * a.topk + slot];
       ok = beta >= 0 && beta < cb;
     } else {
       beta = cb;

@@ -57,11 +57,11 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Historical block count of token t (0 for a token whose sequence or position
-// is out of range).
+// Historical block count of query row t (0 for a token whose sequence or
+// position is out of range).
 __device__ __forceinline__ int hist_blocks(const IndexerArgs& a, int t, int* seq_out) {
-  const int b = a.q_seq[t];
-  const int p = a.q_pos[t];
+  const int b = a.q_seq[t >> a.q_shift];
+  const int p = a.q_pos[t >> a.q_shift];
   *seq_out = b;
   if (b < 0 || b >= a.batch || p < 0) return 0;
   if (p >= a.seq_lens[b] || p >= a.max_pages * kPageTokens) return 0;

@@ -46,6 +46,7 @@ struct AttnArgs {
   float scale_log2;         // softmax_scale * log2(e)
   bool stream_kv;           // non-temporal K/V loads (blocks read about once per call)
   bool kv_fp8;              // one-byte (OCP E4M3) K/V caches
+  bool sel_per_group;       // sel_idx is [n_tok][4][topk] (one set per KV group), else [n_tok][topk]
   float v_scale;            // V = code * v_scale for a one-byte cache (1 for bf16)
   float* part_o;            // used when num_splits > 1
   float* part_lse;
@@ -60,7 +61,8 @@ struct IndexerArgs {
   const int32_t* seq_lens;
   const int32_t* q_seq;
   const int32_t* q_pos;
-  int n_tok;
+  int n_tok;                // query rows (tokens, or tokens x KV groups)
+  int q_shift;              // query row r belongs to token r >> q_shift (0: one row per token, 2: per group)
   int topk;
   int batch;
   int max_pages;

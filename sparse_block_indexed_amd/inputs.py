@@ -174,6 +174,13 @@ def make_workload(spec: WorkloadSpec, seed: int, device="cpu") -> Workload:
                     k_cache=k_cache, v_cache=v_cache, k_idx_cache=k_idx_cache)
 
 
+def grouped_index_queries(n_tok: int, seed: int, device="cpu", lo: int = -4, hi: int = 4) -> torch.Tensor:
+    """One index query per (token, KV group): integers in [lo, hi] as bf16, [n_tok][4][256]."""
+    gen = torch.Generator(device=torch.device(device))
+    gen.manual_seed(seed)
+    return _randint_bf16((n_tok, G, DI), lo, hi, gen, torch.device(device))
+
+
 def config_workload(index: int, device="cpu", seed: Optional[int] = None) -> Workload:
     """One of the five named workloads; the seed defaults to the workload's index."""
     return make_workload(CONFIGS[index], index if seed is None else seed, device)

@@ -23,7 +23,9 @@ MAX_SPLITS = 64
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 EXPORTED = ["sa_status_string", "sa_indexer_topk_workspace_size", "sa_indexer_topk", "sa_indexer_topk_fp8",
             "sa_resolve_num_splits", "sa_sparse_decode", "sa_sparse_decode_fp8kv", "sa_swa_decode",
-            "sa_swa_decode_fp8kv", "sa_merge"]
+            "sa_swa_decode_fp8kv", "sa_merge", "sa_indexer_topk_grouped_workspace_size",
+            "sa_indexer_topk_grouped", "sa_sparse_decode_grouped"]
+FORMAT_BF16, FORMAT_FP8_E4M3 = 0, 1
 
 
 class SAError(RuntimeError):
@@ -69,6 +71,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sa_swa_decode_fp8kv.restype = i32
     lib.sa_swa_decode_fp8kv.argtypes = [vp, vp, vp, f32, f32, PagedDesc, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp,
                                         vp]
+    lib.sa_indexer_topk_grouped_workspace_size.restype = sz
+    lib.sa_indexer_topk_grouped_workspace_size.argtypes = [i32, i32, i32]
+    lib.sa_indexer_topk_grouped.restype = i32
+    lib.sa_indexer_topk_grouped.argtypes = [vp, vp, i32, PagedDesc, vp, vp, i32, i32, vp, vp, sz, vp]
+    lib.sa_sparse_decode_grouped.restype = i32
+    lib.sa_sparse_decode_grouped.argtypes = [vp, vp, vp, i32, f32, f32, PagedDesc, vp, vp, vp, i32, i32, f32, i32,
+                                             vp, vp, vp, vp, vp]
     lib.sa_merge.restype = i32
     lib.sa_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     _lib = lib
@@ -108,8 +117,10 @@ def _desc(page_table: torch.Tensor, seq_lens: torch.Tensor, num_pages: int) -> P
                      int(num_pages))
 
 
-def indexer_workspace_size(n_tok: int, max_pages_per_seq: int, topk: int = MAX_TOPK) -> int:
-    return int(load_library().sa_indexer_topk_workspace_size(n_tok, max_pages_per_seq, topk))
+def indexer_workspace_size(n_tok: int, max_pages_per_seq: int, topk: int = MAX_TOPK, per_group: bool = False) -> int:
+    lib = load_library()
+    fn = lib.sa_indexer_topk_grouped_workspace_size if per_group else lib.sa_indexer_topk_workspace_size
+    return int(fn(n_tok, max_pages_per_seq, topk))
 
 
 def resolve_num_splits(n_tok: int, max_blocks_per_token: int, num_splits: int = 0) -> int:
@@ -121,11 +132,14 @@ def indexer_topk(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk: i
     """Top-k historical blocks per query token (ascending, -1 padded): int32 [n_tok][topk].
 
     k_idx_cache is bf16, or one-byte OCP E4M3 keys (torch.float8_e4m3fn, or
-    their codes as torch.uint8), which go to sa_indexer_topk_fp8."""
+    their codes as torch.uint8), which go to sa_indexer_topk_fp8. A q_idx of
+    shape [n_tok][4][256] (one query per KV group) selects per group through
+    sa_indexer_topk_grouped and returns int32 [n_tok][4][topk]."""
     lib = load_library()
     dev = q_idx.device
     n_tok = q_idx.shape[0]
-    _need(q_idx, "q_idx", torch.bfloat16, dev, (n_tok, DI))
+    per_group = q_idx.dim() == 3
+    _need(q_idx, "q_idx", torch.bfloat16, dev, (n_tok, G, DI) if per_group else (n_tok, DI))
     fp8 = k_idx_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
     if fp8:
         k_idx_cache = k_idx_cache.view(torch.uint8)
@@ -135,17 +149,24 @@ def indexer_topk(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk: i
     _need(q_seq, "q_seq", torch.int32, dev, (n_tok,))
     _need(q_pos, "q_pos", torch.int32, dev, (n_tok,))
     pd = _desc(page_table, seq_lens, k_idx_cache.shape[0])
+    sel_shape = (n_tok, G, topk) if per_group else (n_tok, topk)
     if sel_idx is None:
-        sel_idx = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
-    _need(sel_idx, "sel_idx", torch.int32, dev, (n_tok, topk))
-    need = indexer_workspace_size(n_tok, pd.max_pages_per_seq, topk)
+        sel_idx = torch.empty(sel_shape, dtype=torch.int32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, dev, sel_shape)
+    need = indexer_workspace_size(n_tok, pd.max_pages_per_seq, topk, per_group)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev)
-    fn = lib.sa_indexer_topk_fp8 if fp8 else lib.sa_indexer_topk
-    st = fn(_ptr(q_idx), _ptr(k_idx_cache), pd, _ptr(q_seq), _ptr(q_pos), n_tok, topk, _ptr(sel_idx),
-            _ptr(workspace), workspace.numel(), _stream(stream))
-    _check("sa_indexer_topk_fp8" if fp8 else "sa_indexer_topk", st)
+    tail = (pd, _ptr(q_seq), _ptr(q_pos), n_tok, topk, _ptr(sel_idx), _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    if per_group:
+        name = "sa_indexer_topk_grouped"
+        st = lib.sa_indexer_topk_grouped(_ptr(q_idx), _ptr(k_idx_cache), FORMAT_FP8_E4M3 if fp8 else FORMAT_BF16,
+                                         *tail)
+    else:
+        name = "sa_indexer_topk_fp8" if fp8 else "sa_indexer_topk"
+        st = getattr(lib, name)(_ptr(q_idx), _ptr(k_idx_cache), *tail)
+    _check(name, st)
     return sel_idx
 
 
@@ -205,18 +226,25 @@ def sparse_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, sel_i
                   v_scale: Optional[float] = None):
     """Attention over selected + current blocks. Returns (out, out_lse) or, with
     partials_only, (part_o, part_lse) of the resolved number of splits. One-byte
-    caches (with k_scale, v_scale) go to sa_sparse_decode_fp8kv."""
+    caches (with k_scale, v_scale) go to sa_sparse_decode_fp8kv. A sel_idx of
+    shape [n_tok][4][topk] (one set per KV group) goes to sa_sparse_decode_grouped."""
     lib = load_library()
     dev, n_tok, fp8, k_cache, v_cache = _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos, k_scale, v_scale)
-    topk = sel_idx.shape[1]
-    _need(sel_idx, "sel_idx", torch.int32, dev, (n_tok, topk))
+    per_group = sel_idx.dim() == 3
+    topk = sel_idx.shape[-1]
+    _need(sel_idx, "sel_idx", torch.int32, dev, (n_tok, G, topk) if per_group else (n_tok, topk))
     pd = _desc(page_table, seq_lens, k_cache.shape[0])
     S = resolve_num_splits(n_tok, topk + 1, num_splits)
     out, out_lse, part_o, part_lse = _decode_buffers(n_tok, S, dev, out, out_lse, part_o, part_lse,
                                                      want_out=not partials_only)
     tail = (pd, _ptr(q_seq), _ptr(q_pos), _ptr(sel_idx), n_tok, topk, float(softmax_scale), int(num_splits),
             _ptr(part_o), _ptr(part_lse), None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
-    if fp8:
+    if per_group:
+        name = "sa_sparse_decode_grouped"
+        st = lib.sa_sparse_decode_grouped(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                          FORMAT_FP8_E4M3 if fp8 else FORMAT_BF16,
+                                          float(k_scale) if fp8 else 1.0, float(v_scale) if fp8 else 1.0, *tail)
+    elif fp8:
         name = "sa_sparse_decode_fp8kv"
         st = lib.sa_sparse_decode_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale), *tail)
     else:

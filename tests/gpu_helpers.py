@@ -101,6 +101,31 @@ class OracleView:
         vc = I.bf16_bits(wl.v_cache.index_select(0, idx))
         return O.attend_positions(q, kc, vc, compact, positions, scale)
 
+    def selection_grouped(self, t, q_idx_groups, topk=512):
+        """Per-group selections [4][topk] of token t for index queries [n_tok][4][256]."""
+        b, p = int(self.wl.q_seq[t]), int(self.wl.q_pos[t])
+        keys = self.keys(b, p // 8)
+        qg = q_idx_groups[t]
+        return np.stack([O.indexer_topk_token(O.bf16_to_f64(I.bf16_bits(qg[g])), keys, topk) for g in range(4)])
+
+    def sparse_grouped(self, t, sels, scale=SCALE):
+        wl = self.wl
+        b, p = int(wl.q_seq[t]), int(wl.q_pos[t])
+        row = wl.page_table[b]
+        positions = [O.sparse_token_positions(np.asarray(sels[g]), p) for g in range(4)]
+        logical = np.unique(np.concatenate(positions) // 64)
+        idx = torch.as_tensor(row[logical].astype(np.int64), device=wl.k_cache.device)
+        compact = np.full(row.shape[0], -1, dtype=np.int64)
+        compact[logical] = np.arange(len(logical))
+        q = O.bf16_to_f64(I.bf16_bits(wl.q[t]))
+        if self.kv_fp8 is not None:
+            k8, v8, ks, vs = self.kv_fp8
+            kc, vc = k8.index_select(0, idx).cpu().numpy(), v8.index_select(0, idx).cpu().numpy()
+            return O.attend_positions_by_group(q, kc, vc, compact, positions, scale, fp8_scales=(ks, vs))
+        kc = I.bf16_bits(wl.k_cache.index_select(0, idx))
+        vc = I.bf16_bits(wl.v_cache.index_select(0, idx))
+        return O.attend_positions_by_group(q, kc, vc, compact, positions, scale)
+
     def sparse(self, t, sel, scale=SCALE):
         return self.attention(t, O.sparse_token_positions(np.asarray(sel), int(self.wl.q_pos[t])), scale)
 

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ["sa_indexer_topk", "sa_indexer_topk_fp8", "sa_sparse_decode", "sa_sparse_decode_fp8kv",
               "sa_swa_decode", "sa_swa_decode_fp8kv", "sa_merge", "sa_indexer_topk_workspace_size",
-              "sa_status_string", "sa_resolve_num_splits"]:
+              "sa_status_string", "sa_resolve_num_splits", "sa_indexer_topk_grouped",
+              "sa_indexer_topk_grouped_workspace_size", "sa_sparse_decode_grouped"]:
         assert n in names
 
 
@@ -170,6 +171,41 @@ def test_binding_checks_fp8_cache_arguments():
         ops._check_attn_inputs(q, kb, kb, i, i, 1.0, None)
     dev, n, fp8, k, v = ops._check_attn_inputs(q, k8.view(torch.float8_e4m3fn), k8, i, i, 0.5, 0.25)
     assert fp8 and n == 1 and k.dtype == torch.uint8 and v.dtype == torch.uint8
+
+
+def test_grouped_entry_points_validation(lib):
+    """Per-KV-group selection: the workspace covers 4 query rows per token; bad
+    formats, sizes and buffers are refused before any launch."""
+    from sparse_block_indexed_amd import ops
+    d = _desc(ops)
+    assert lib.sa_indexer_topk_grouped_workspace_size(3, 16, 512) == lib.sa_indexer_topk_workspace_size(12, 16, 512)
+    assert lib.sa_indexer_topk_grouped_workspace_size(0, 16, 512) == 0
+    assert lib.sa_indexer_topk_grouped_workspace_size(1 << 29, 16, 512) == 0
+    ws = lib.sa_indexer_topk_grouped_workspace_size(4, 16, 512)
+    f = lib.sa_indexer_topk_grouped
+    assert f(None, None, 0, d, None, None, 0, 512, None, None, 0, None) == ops.SA_OK
+    assert f(P, P, 2, d, P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED           # key format
+    assert f(P, P, -1, d, P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, 0, d, P, P, 4, 512, P, P, ws - 1, None) == ops.SA_ERR_WORKSPACE
+    assert f(P, P, 1, d, P, P, 4, 512, P, P, lib.sa_indexer_topk_workspace_size(4, 16, 512), None) \
+        == ops.SA_ERR_WORKSPACE                                                            # per-token size is short
+    assert f(P, P, 0, d, P, P, 4, 0, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, 0, d, P, P, 1 << 29, 512, P, P, ws, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, None, 0, d, P, P, 4, 512, P, P, ws, None) == ops.SA_ERR_INVALID_ARG
+    g = lib.sa_sparse_decode_grouped
+    one = ctypes.c_float(1.0)
+
+    def call(fmt=0, ks=one, vs=one, sel=P, n=4, topk=512, out=P):
+        return g(P, P, P, fmt, ks, vs, d, P, P, sel, n, topk, ctypes.c_float(0.07), 1, None, None, out, None, None)
+
+    assert g(None, None, None, 0, one, one, d, None, None, None, 0, 512, ctypes.c_float(0.07), 0, None, None,
+             None, None, None) == ops.SA_OK
+    assert call(fmt=3) == ops.SA_ERR_UNSUPPORTED
+    assert call(sel=None) == ops.SA_ERR_INVALID_ARG
+    assert call(topk=513) == ops.SA_ERR_UNSUPPORTED
+    assert call(fmt=1, vs=ctypes.c_float(0.0)) == ops.SA_ERR_INVALID_ARG                  # fp8 checks its scales
+    assert call(n=1 << 29) == ops.SA_ERR_UNSUPPORTED
+    assert call(out=None) == ops.SA_ERR_INVALID_ARG
 
 
 def test_swa_and_merge_validation(lib):

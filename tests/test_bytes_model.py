@@ -32,3 +32,22 @@ def test_launch_bytes_count_distinct_blocks():
     # distinct blocks {0, 3, 5, 12}: 4 units x 4 groups x (K + V) x 3072 B
     expect = 4 * 4 * 2 * 3072 + 2 * 64 * 192 * 2 * 2 + sel.size * 4 + 2 * 64 * 4
     assert B.sparse_attention_bytes(q_seq, q_pos, sel) == expect
+
+
+def test_grouped_launch_bytes_count_distinct_blocks_per_group():
+    q_seq = np.array([0, 0])
+    q_pos = np.array([100, 101])        # current block 12 for both
+    sel = np.full((2, 4, 3), -1)
+    sel[0, 0, :2] = [0, 3]
+    sel[1, 0, :2] = [3, 5]               # group 0: {0, 3, 5, 12} -> 4 units
+    sel[0, 1, :1] = [7]                  # group 1: {7, 12} -> 2 units
+    # groups 2, 3: current block only -> 1 unit each
+    units = 4 + 2 + 1 + 1
+    expect = units * 2 * 3072 + 2 * 64 * 192 * 2 * 2 + sel.size * 4 + 2 * 64 * 4
+    assert B.sparse_attention_bytes_grouped(q_seq, q_pos, sel) == expect
+    # one-byte caches halve the unit
+    assert B.sparse_attention_bytes_grouped(q_seq, q_pos, sel, kv_bytes=1) == expect - units * 2 * 1536
+    # all groups choosing alike: the shared form's count
+    same = np.repeat(np.array([[0, 3, -1], [3, 5, -1]])[:, None, :], 4, axis=1)
+    assert B.sparse_attention_bytes_grouped(q_seq, q_pos, same) == \
+        B.sparse_attention_bytes(q_seq, q_pos, same[:, 0]) + 2 * 3 * 3 * 4
