@@ -144,6 +144,154 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
                       f"oracle, {t_cpu:.1f} s of CPU time, host copies excluded"}
 
 
+def capture(fn, reps: int = 1):
+    """A HIP graph of `reps` back-to-back calls of fn (warmed up on a side stream first)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(run_step, steps: int, eager: bool) -> float:
+    """Wall-clock ms per step over exactly `steps` back-to-back steps: eager calls,
+    or graph replays of GRAPH_STEPS steps (plus single-step replays for the rest)."""
+    import torch
+    if not eager:
+        g_one, g_many = capture(run_step), capture(run_step, GRAPH_STEPS)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if eager:
+        for _ in range(steps):
+            run_step()
+    else:
+        for _ in range(steps // GRAPH_STEPS):
+            g_many.replay()
+        for _ in range(steps % GRAPH_STEPS):
+            g_one.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_phase(fn, steps: int, eager: bool, stream, reps: int = 5) -> float:
+    """Mean ms per call of one phase: HIP events on the launch stream around
+    `reps` back-to-back calls (one graph replay, or eager calls)."""
+    import torch
+    runner = (lambda: [fn() for _ in range(reps)]) if eager else capture(fn, reps).replay
+    runner()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(2, steps // reps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        runner()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    return float(np.mean(times))
+
+
+NAMES = {0: "decode_8k_b1", 1: "mtp_verify_128k_b64", 2: "swa_decode_32k_b64", 3: "decode_1m_b4",
+         4: "prefill_chunk_16k_at_112k"}
+
+
+def layer_group(args, wl, dev):
+    """One hybrid layer group per step (SGLang blog, "Hybrid Attention": three
+    sliding-window layers per sparse layer): three window-512 layers, then the
+    sparse layer (indexer + top-512 + attention). Each layer has its own seeded
+    Q and caches over the same sequences, as the layers of a model do. The
+    layers' calls run back to back from one captured graph; in a model the
+    other ops of each layer sit between them, which is why the group is a
+    schedule of four calls and not one fused kernel."""
+    import torch
+    from sparse_block_indexed_amd import bytes_model as B
+    from sparse_block_indexed_amd import inputs as I
+    from sparse_block_indexed_amd import ops
+    W = args.workload
+    if args.fp8_kv or args.per_group_selection or args.fp8_index_keys:
+        raise SystemExit("--layer-group runs the bf16 layers only")
+    n_tok, topk, window = wl.n_tok, 512, 512
+    pt, sl, qs, qp = wl.device_ints(dev)
+    layers = [I.layer_inputs(wl, seed=7000 + 10 * W + i) for i in range(3)] + [wl]
+    Sw = ops.resolve_num_splits(n_tok, window // 8 + 2, args.num_splits)
+    Ss = ops.resolve_num_splits(n_tok, topk + 1, args.num_splits)
+    f32 = dict(dtype=torch.float32, device=dev)
+    outs = [torch.empty((n_tok, 64, 192), dtype=torch.bfloat16, device=dev) for _ in layers]
+    lses = [torch.empty((n_tok, 64), **f32) for _ in layers]
+    pw = (torch.empty((n_tok, Sw, 64, 192), **f32), torch.empty((n_tok, Sw, 64), **f32)) if Sw > 1 else (None, None)
+    ps = (torch.empty((n_tok, Ss, 64, 192), **f32), torch.empty((n_tok, Ss, 64), **f32)) if Ss > 1 else (None, None)
+    sel = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def swa(i):
+        L = layers[i]
+        ops.swa_decode(L.q, L.k_cache, L.v_cache, pt, sl, qs, qp, window, SCALE, num_splits=Sw, out=outs[i],
+                       out_lse=lses[i], part_o=pw[0], part_lse=pw[1])
+
+    def indexer():
+        ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
+
+    def sparse():
+        ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=Ss, out=outs[3],
+                          out_lse=lses[3], part_o=ps[0], part_lse=ps[1])
+
+    def run_group():
+        for i in range(3):
+            swa(i)
+        indexer()
+        sparse()
+
+    for _ in range(args.warmup):
+        run_group()
+    torch.cuda.synchronize()
+    ms = time_steps(run_group, args.steps, args.eager)
+    ms_eager = time_steps(run_group, args.steps, True) if not args.eager else ms
+    phase_ms = {"swa_decode": time_phase(lambda: swa(0), args.steps, args.eager, stream),
+                "indexer_topk": time_phase(indexer, args.steps, args.eager, stream),
+                "sparse_decode": time_phase(sparse, args.steps, args.eager, stream)}
+    run_group()
+    torch.cuda.synchronize()
+    sel_host = sel.cpu().numpy()
+    nbytes = {"swa_decode": B.swa_attention_bytes(wl.q_seq, wl.q_pos, window),
+              "indexer_topk": B.indexer_topk_bytes(wl.q_seq, wl.q_pos, topk),
+              "sparse_decode": B.sparse_attention_bytes(wl.q_seq, wl.q_pos, sel_host)}
+    count = {"swa_decode": 3, "indexer_topk": 1, "sparse_decode": 1}
+    dominant = max(phase_ms, key=lambda k: count[k] * phase_ms[k])
+    achieved = nbytes[dominant] / (phase_ms[dominant] * 1e-3) / 1e9
+    kname = {"swa_decode": "attention_kernel<true, bf16>%s (sa_swa_decode)" % (" + merge_kernel" if Sw > 1 else ""),
+             "indexer_topk": "sa_indexer_topk (score_kernel + select)",
+             "sparse_decode": "attention_kernel<false, bf16>%s (sa_sparse_decode)" % (" + merge_kernel" if Ss > 1 else "")}
+    group_bytes = sum(count[k] * nbytes[k] for k in nbytes)
+    return {
+        "metric": f"{NAMES[W]} hybrid layer group (3 window + 1 sparse layer) query-tokens/s; achieved HBM GB/s",
+        "value": n_tok / (ms * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": NAMES[W] + "_layer_group", "layers": "3 x window 512 + 1 x sparse top-512",
+                   "batch": wl.batch, "query_tokens": n_tok, "num_splits_window": Sw, "num_splits_sparse": Ss,
+                   "kv_cache": "bf16", "launch": "eager" if args.eager else "hip_graph"},
+        "eager_ms_per_step": ms_eager,
+        "achieved_hbm_gbps": group_bytes / (ms * 1e-3) / 1e9,
+        "step_breakdown_ms": {"swa_decode x3": 3 * phase_ms["swa_decode"],
+                              "indexer_topk": phase_ms["indexer_topk"],
+                              "sparse_decode": phase_ms["sparse_decode"]},
+        "per_call_ms": phase_ms,
+        "algorithmic_bytes": {k: count[k] * nbytes[k] for k in nbytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": kname[dominant]},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +312,9 @@ def main():
                          "(k_scale 1/32, v_scale 1/16)")
     ap.add_argument("--per-group-selection", action="store_true",
                     help="one index query and one top-512 set per (token, KV group) instead of per token")
+    ap.add_argument("--layer-group", action="store_true",
+                    help="one step = a hybrid layer group: 3 sliding-window layers + 1 sparse layer, each with its "
+                         "own Q and caches over the workload's sequences")
     ap.add_argument("--eager", action="store_true",
                     help="issue every call from Python instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -195,6 +346,9 @@ def main():
     ops.load_library()
     W = args.workload
     wl = I.config_workload(W, device=dev)
+    if args.layer_group:
+        print(json.dumps(layer_group(args, wl, dev)), flush=True)
+        return
     pt, sl, qs, qp = wl.device_ints(dev)
     kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if args.fp8_index_keys else wl.k_idx_cache
     per_group = args.per_group_selection
@@ -239,73 +393,14 @@ def main():
         run_step()
     torch.cuda.synchronize()
 
-    if args.eager:
-        # every call issued from Python: small steps include the host's launch time
-        launch_step = run_step
-        phases = {"indexer_topk": run_indexer, "attention": run_attention}
-    else:
-        # The step and each phase are captured once as HIP graphs and replayed:
-        # every replay runs all kernels of the step on the same inputs; only the
-        # host's per-call argument handling is gone.
-        def capture(fn, reps=1):
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                fn()
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(reps):
-                    fn()
-            torch.cuda.synchronize()
-            return g
-
-        # a served decode forward replays many layers from one graph; GRAPH_STEPS
-        # steps per replay keep the graph launch's fixed host cost out of the
-        # per-step figure in the same way
-        g_one = capture(run_step)
-        g_many = capture(run_step, GRAPH_STEPS)
-        launch_step = g_one.replay
-        phases = {"indexer_topk": run_indexer, "attention": run_attention}
-    if window is not None:
-        del phases["indexer_topk"]
-
-    # exactly args.steps whole steps, back to back: the throughput figure
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if args.eager:
-        for i in range(args.steps):
-            launch_step()
-    else:
-        for i in range(args.steps // GRAPH_STEPS):
-            g_many.replay()
-        for i in range(args.steps % GRAPH_STEPS):
-            g_one.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # per-phase duration with HIP events on the launch stream: REPS back-to-back
-    # launches of one phase per timed interval (one graph replay, or REPS eager
-    # calls), so the interval holds that phase's kernels only
-    REPS = 5
-    phase_ms = {}
-    for name, fn in phases.items():
-        runner = (lambda f=fn: [f() for _ in range(REPS)]) if args.eager else capture(fn, REPS).replay
-        runner()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(max(2, args.steps // REPS)):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            runner()
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1) / REPS)
-        phase_ms[name] = float(np.mean(times))
-    idx_ms = phase_ms.get("indexer_topk", 0.0)
-    attn_ms = phase_ms["attention"]
+    # The step is captured as HIP graphs and replayed (GRAPH_STEPS steps per
+    # replay, as a served decode forward replays its layers from one graph):
+    # every replay runs all kernels of the step on the same inputs; only the
+    # host's per-call argument handling is gone. --eager issues every call.
+    launch_step = run_step if args.eager else capture(run_step).replay
+    ms_per_step = time_steps(run_step, args.steps, args.eager)
+    idx_ms = time_phase(run_indexer, args.steps, args.eager, stream) if window is None else 0.0
+    attn_ms = time_phase(run_attention, args.steps, args.eager, stream)
     # leave the step's own results in sel / out for the byte counts below
     run_step()
     torch.cuda.synchronize()
@@ -343,8 +438,7 @@ def main():
         attn_bytes = B.swa_attention_bytes(wl.q_seq, wl.q_pos, window, kv_bytes=kvb)
         idx_bytes, idx_flops = 0, 0
         attn_flops = B.swa_attention_flops(wl.q_pos, window)
-    names = {0: "decode_8k_b1", 1: "mtp_verify_128k_b64", 2: "swa_decode_32k_b64", 3: "decode_1m_b4",
-             4: "prefill_chunk_16k_at_112k"}
+    names = NAMES
     config = {"workload": names[W], "batch": wl.batch, "query_tokens": n_tok,
               "context": (f"uniform [{wl.spec.seq_len_range[0]}, {wl.spec.seq_len_range[1]}]"
                           if wl.spec.seq_len_range else str(sorted(set(int(x) for x in wl.seq_lens)))),

@@ -174,6 +174,23 @@ def make_workload(spec: WorkloadSpec, seed: int, device="cpu") -> Workload:
                     k_cache=k_cache, v_cache=v_cache, k_idx_cache=k_idx_cache)
 
 
+def layer_inputs(wl: Workload, seed: int) -> Workload:
+    """Another layer over the same sequences: the page table, lengths and query
+    positions of ``wl``, with its own seeded Q, K/V caches, index queries and
+    index keys (each layer of a model has its own caches)."""
+    dev = wl.q.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    spec = wl.spec
+    return dataclasses.replace(
+        wl, seed=seed,
+        q=_randn_bf16(tuple(wl.q.shape), gen, dev),
+        q_idx=_randint_bf16(tuple(wl.q_idx.shape), spec.idx_lo, spec.idx_hi, gen, dev),
+        k_cache=_randn_bf16(tuple(wl.k_cache.shape), gen, dev, chunk_rows=1024),
+        v_cache=_randn_bf16(tuple(wl.v_cache.shape), gen, dev, chunk_rows=1024),
+        k_idx_cache=_randint_bf16(tuple(wl.k_idx_cache.shape), spec.idx_lo, spec.idx_hi, gen, dev))
+
+
 def grouped_index_queries(n_tok: int, seed: int, device="cpu", lo: int = -4, hi: int = 4) -> torch.Tensor:
     """One index query per (token, KV group): integers in [lo, hi] as bf16, [n_tok][4][256]."""
     gen = torch.Generator(device=torch.device(device))

@@ -6,6 +6,7 @@ only: no allocation, no memset, no synchronisation inside a call.
 """
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -132,3 +133,73 @@ def test_config1_step_graph_replays_match_eager():
     _say("graph config 1")
     wl = I.config_workload(1, device="cuda")
     _graph_vs_eager(wl, 0, replays=2)
+
+
+def test_hybrid_layer_group_graph():
+    """Three window layers and one sparse layer, each with its own Q and caches
+    over the same sequences, captured as one graph: every replay equals each
+    layer's own eager call bit for bit, and two layers agree with the oracle."""
+    _say("graph hybrid layer group")
+    from gpu_helpers import OracleView, assert_close_outputs, bf16_to_np
+    from sparse_block_indexed_amd import ops
+    wl = I.make_workload(SMALL, seed=73, device="cuda")
+    layers = [I.layer_inputs(wl, seed=500 + i) for i in range(3)] + [wl]
+    pt, sl, qs, qp = wl.device_ints("cuda")
+    n = wl.n_tok
+    S = 2
+    outs = [torch.empty((n, 64, 192), dtype=torch.bfloat16, device="cuda") for _ in layers]
+    lses = [torch.empty((n, 64), dtype=torch.float32, device="cuda") for _ in layers]
+    po = torch.empty((n, S, 64, 192), dtype=torch.float32, device="cuda")
+    pl = torch.empty((n, S, 64), dtype=torch.float32, device="cuda")
+    sel = torch.empty((n, 512), dtype=torch.int32, device="cuda")
+    ws = torch.empty(ops.indexer_workspace_size(n, wl.max_pages_per_seq, 512), dtype=torch.uint8, device="cuda")
+
+    def group():
+        for i in range(3):
+            L = layers[i]
+            ops.swa_decode(L.q, L.k_cache, L.v_cache, pt, sl, qs, qp, 512, SCALE, num_splits=S, out=outs[i],
+                           out_lse=lses[i], part_o=po, part_lse=pl)
+        ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, 512, sel_idx=sel, workspace=ws)
+        ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=S, out=outs[3],
+                          out_lse=lses[3], part_o=po, part_lse=pl)
+
+    # each layer on its own, eagerly, into fresh buffers
+    ref = []
+    for i in range(3):
+        L = layers[i]
+        ref.append(ops.swa_decode(L.q, L.k_cache, L.v_cache, pt, sl, qs, qp, 512, SCALE, num_splits=S))
+    ref_sel = ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, 512)
+    ref.append(ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, ref_sel, SCALE, num_splits=S))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        group()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        group()
+    for r in range(3):
+        for t in outs + lses:
+            t.fill_(float("nan"))
+        ops.swa_decode(layers[1].q, layers[1].k_cache, layers[1].v_cache, pt, sl, qs, qp, 64, SCALE)   # eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sel, ref_sel)
+        for i in range(4):
+            assert torch.equal(outs[i], ref[i][0]) and torch.equal(lses[i], ref[i][1]), f"replay {r} layer {i}"
+    # the layers really differ, and layer 1 (window) and layer 3 (sparse) match the oracle
+    assert not torch.equal(outs[0], outs[1])
+    ov1, ov3 = OracleView(layers[1]), OracleView(wl)
+    toks = range(0, n, 5)
+    r1 = [ov1.swa(t) for t in toks]
+    assert_close_outputs(bf16_to_np(outs[1][list(toks)]), lses[1][list(toks)].cpu().numpy(),
+                         np.stack([x[0] for x in r1]), np.stack([x[1] for x in r1]), "group window layer")
+    sel_h = sel.cpu().numpy()
+    r3 = [ov3.sparse(t, sel_h[t]) for t in toks]
+    for t in toks:
+        assert sel_h[t].tolist() == ov3.selection(t).tolist()
+    assert_close_outputs(bf16_to_np(outs[3][list(toks)]), lses[3][list(toks)].cpu().numpy(),
+                         np.stack([x[0] for x in r3]), np.stack([x[1] for x in r3]), "group sparse layer")
