@@ -596,10 +596,14 @@ __global__ __launch_bounds__(kThreads) void collect_kernel(IndexerArgs a) {
 constexpr int kFinalThreads = 512;
 
 constexpr int kTieCap = 2048;   // threshold-bin entries resolved in LDS
+constexpr int kRankMax = 256;   // threshold bins up to this size are resolved by ranking
 
-struct FinalizeLds {
-  uint32_t tzk[kTieCap];    // keys of the threshold bin
-  uint32_t tzi[kTieCap];    // their block ids
+__device__ __forceinline__ uint64_t tz_entry(uint32_t key, uint32_t beta) { return (uint64_t)key << 32 | (uint32_t)~beta; }
+__device__ __forceinline__ uint32_t tz_key(uint64_t e) { return (uint32_t)(e >> 32); }
+__device__ __forceinline__ uint32_t tz_block(uint64_t e) { return ~(uint32_t)e; }
+
+struct alignas(16) FinalizeLds {
+  uint64_t tz[kTieCap];     // threshold-bin entries: key << 32 | ~block id (a larger entry ranks first)
   uint32_t h[kHistBins];
   uint32_t tmp[kFinalThreads / 64];
   uint32_t res[2];
@@ -700,14 +704,23 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   const bool fused = ncand <= kFuseLimit;
   // a short history's scores are held in registers from here on
   constexpr int kPer = kFuseLimit / kFinalThreads;
+  const int jmax = (ncand + kFinalThreads - 1) / kFinalThreads;   // steps j that hold scores (uniform)
   uint32_t kv[kPer];
   if (fused) {
+    // every load of a step is issued (past the history they re-read its last
+    // score), so all of them are in flight at once
     const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+    float sv[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int beta = j * kFinalThreads + (int)threadIdx.x;
-      kv[j] = beta < ncand ? score_key(srow[beta]) : 0u;
+    for (int j0 = 0; j0 < kPer; j0 += 8) {   // groups of 8 steps, each group's loads unconditional
+      if (j0 < jmax) {
+#pragma unroll
+        for (int j = j0; j < j0 + 8; ++j) sv[j] = srow[min(j * kFinalThreads + (int)threadIdx.x, ncand - 1)];
+      }
     }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      kv[j] = j < jmax && j * kFinalThreads + (int)threadIdx.x < ncand ? score_key(sv[j]) : 0u;
     for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
   } else {
     for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
@@ -723,8 +736,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   if (fused) {   // the score pass built no histogram for short histories
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int beta = j * kFinalThreads + (int)threadIdx.x;
-      if (beta < ncand) atomicAdd(&s.h[kv[j] >> 21], 1u);
+      if (j < jmax) {
+        const int beta = j * kFinalThreads + (int)threadIdx.x;
+        if (beta < ncand) atomicAdd(&s.h[kv[j] >> 21], 1u);
+      }
     }
     __syncthreads();
   }
@@ -744,16 +759,52 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
     } else if (bin == b1) {
       const uint32_t slot = atomicAdd(&s.n_tz, 1u);
       if (slot < (uint32_t)kTieCap) {
-        s.tzk[slot] = key;
-        s.tzi[slot] = beta;
+        s.tz[slot] = tz_entry(key, beta);
       }
     }
   };
   if (fused) {
+    // A wave holds 64 consecutive block ids per j: its ballot of "above the
+    // threshold bin" is exactly two bitmap words, and the threshold-bin keys
+    // take one counter update per wave.
+    // Lane j keeps the two words of step j; they are stored once at the end.
+    const int lane = threadIdx.x & 63;
+    uint32_t n_wave = 0;   // this wave's threshold-bin keys (first pass: count)
+    uint32_t word_lo = 0, word_hi = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int beta = j * kFinalThreads + (int)threadIdx.x;
-      if (beta < ncand) classify(kv[j], (uint32_t)beta);
+      if (j < jmax) {
+        const bool valid = j * kFinalThreads + (int)threadIdx.x < ncand;
+        const uint32_t bin = kv[j] >> 21;
+        const uint64_t above_mask = __ballot(valid && bin > b1);
+        word_lo = lane == j ? (uint32_t)above_mask : word_lo;
+        word_hi = lane == j ? (uint32_t)(above_mask >> 32) : word_hi;
+        n_wave += (uint32_t)__popcll(__ballot(valid && bin == b1));
+      }
+    }
+    if (lane < jmax) {
+      const int w = (lane * kFinalThreads + (int)(threadIdx.x - lane)) >> 5;
+      if (w < nw) sel_bm[w] = word_lo;
+      if (w + 1 < nw) sel_bm[w + 1] = word_hi;
+    }
+    if (n_wave != 0u) {   // second pass: slots base + rank within the wave
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s.n_tz, n_wave);
+      base = __shfl(base, 0);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        if (j < jmax) {
+          const int beta = j * kFinalThreads + (int)threadIdx.x;
+          const bool tz = beta < ncand && (kv[j] >> 21) == b1;
+          const uint64_t tz_mask = __ballot(tz);
+          const uint32_t slot = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(tz_mask >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)tz_mask, 0u));
+          if (tz && slot < (uint32_t)kTieCap) {
+            s.tz[slot] = tz_entry(kv[j], (uint32_t)beta);
+          }
+          base += (uint32_t)__popcll(tz_mask);
+        }
+      }
     }
   } else {
     for (uint32_t i = threadIdx.x; i < n_listed; i += kFinalThreads) {
@@ -762,50 +813,75 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
     }
   }
   __syncthreads();
-  // exact k-th key inside the threshold bin: two more radix levels
   const int m = (int)min(s.n_tz, (uint32_t)kTieCap);
   const uint32_t need = (uint32_t)k - above;
-  uint32_t prefix = b1 << 21;
-  uint32_t gt_in_bin = 0;
-  {
-    const int shifts[2] = {10, 0};
-    const int widths[2] = {11, 10};
-    for (int lvl = 0; lvl < 2; ++lvl) {
-      const int sh = shifts[lvl];
-      const int nb = 1 << widths[lvl];
-      const int hs = sh + widths[lvl];
-      for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
-      __syncthreads();
-      for (int i = threadIdx.x; i < m; i += kFinalThreads) {
-        const uint32_t key = s.tzk[i];
-        if ((key >> hs) == (prefix >> hs)) atomicAdd(&s.h[(key >> sh) & (uint32_t)(nb - 1)], 1u);
+  // contiguous range of block ids [bb0, bb1) of this thread (so that every
+  // thread has bits to walk even for short histories)
+  const int perb = (ncand + kFinalThreads - 1) / kFinalThreads;
+  const int bb0 = min(ncand, (int)threadIdx.x * perb), bb1 = min(ncand, bb0 + perb);
+  const int wlo = bb0 >> 5, whi = bb1 > bb0 ? ((bb1 - 1) >> 5) + 1 : wlo;
+  auto range_bits = [&](const uint32_t* bm, int w) -> uint32_t {
+    const int lo = max(bb0 - 32 * w, 0), hi = min(bb1 - 32 * w, 32);   // 0 <= lo < hi <= 32
+    const uint32_t mhi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
+    return bm[w] & mhi & ~((1u << lo) - 1u);
+  };
+  if (m <= kRankMax) {
+    // Few keys in the threshold bin: a key is chosen iff fewer than `need` of
+    // them come before it (a larger key, or an equal key of a lower block).
+    const int m2 = m & ~1;
+    for (int i = threadIdx.x; i < m; i += kFinalThreads) {
+      const uint64_t e = s.tz[i];
+      uint32_t rank = 0;
+#pragma unroll 4
+      for (int j = 0; j < m2; j += 2) {
+        const ulonglong2 ej = *reinterpret_cast<const ulonglong2*>(&s.tz[j]);
+        rank += ej.x > e ? 1u : 0u;
+        rank += ej.y > e ? 1u : 0u;
       }
-      __syncthreads();
-      select_bin<kFinalThreads>(s.h, nb, need - gt_in_bin, s.tmp, s.res);
-      prefix |= s.res[0] << sh;
-      gt_in_bin += s.res[1];
-      __syncthreads();
+      if (m2 < m) rank += s.tz[m2] > e ? 1u : 0u;
+      const uint32_t beta = tz_block(e);
+      if (rank < need) atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
     }
-  }
-  const uint32_t tau = prefix;
-  const uint32_t need_eq = need - min(gt_in_bin, need);
-  for (int i = threadIdx.x; i < m; i += kFinalThreads) {
-    const uint32_t key = s.tzk[i], beta = s.tzi[i];
-    if (key > tau) atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
-    else if (key == tau) atomicOr(&eq_bm[beta >> 5], 1u << (beta & 31));
-  }
-  __syncthreads();
-  // contiguous word range of this thread
-  const int per = (nw + kFinalThreads - 1) / kFinalThreads;
-  const int w0 = min(nw, (int)threadIdx.x * per), w1 = min(nw, w0 + per);
-  // ties at tau: the first need_eq in block order
-  {
+    __syncthreads();
+  } else {
+    // exact k-th key inside the threshold bin: two more radix levels
+    uint32_t prefix = b1 << 21;
+    uint32_t gt_in_bin = 0;
+    {
+      const int shifts[2] = {10, 0};
+      const int widths[2] = {11, 10};
+      for (int lvl = 0; lvl < 2; ++lvl) {
+        const int sh = shifts[lvl];
+        const int nb = 1 << widths[lvl];
+        const int hs = sh + widths[lvl];
+        for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
+        __syncthreads();
+        for (int i = threadIdx.x; i < m; i += kFinalThreads) {
+          const uint32_t key = tz_key(s.tz[i]);
+          if ((key >> hs) == (prefix >> hs)) atomicAdd(&s.h[(key >> sh) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        select_bin<kFinalThreads>(s.h, nb, need - gt_in_bin, s.tmp, s.res);
+        prefix |= s.res[0] << sh;
+        gt_in_bin += s.res[1];
+        __syncthreads();
+      }
+    }
+    const uint32_t tau = prefix;
+    const uint32_t need_eq = need - min(gt_in_bin, need);
+    for (int i = threadIdx.x; i < m; i += kFinalThreads) {
+      const uint32_t key = tz_key(s.tz[i]), beta = tz_block(s.tz[i]);
+      if (key > tau) atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
+      else if (key == tau) atomicOr(&eq_bm[beta >> 5], 1u << (beta & 31));
+    }
+    __syncthreads();
+    // ties at tau: the first need_eq in block order
     uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(eq_bm[w]);
+    for (int w = wlo; w < whi; ++w) cnt += (uint32_t)__popc(range_bits(eq_bm, w));
     uint32_t tot;
     uint32_t before = block_prefix_exclusive<kFinalThreads>(cnt, s.tmp, &tot);
-    for (int w = w0; w < w1 && before < need_eq; ++w) {
-      uint32_t bits = eq_bm[w];
+    for (int w = wlo; w < whi && before < need_eq; ++w) {
+      uint32_t bits = range_bits(eq_bm, w);
       uint32_t take = 0;
       while (bits != 0u && before < need_eq) {
         const uint32_t low = bits & (0u - bits);
@@ -813,18 +889,18 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
         bits ^= low;
         ++before;
       }
-      if (take) sel_bm[w] |= take;   // this thread owns word w
+      if (take) atomicOr(&sel_bm[w], take);   // a word can straddle two threads' ranges
     }
+    __syncthreads();
   }
-  __syncthreads();
   // ascending output
   {
     uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(sel_bm[w]);
+    for (int w = wlo; w < whi; ++w) cnt += (uint32_t)__popc(range_bits(sel_bm, w));
     uint32_t tot;
     uint32_t pos = block_prefix_exclusive<kFinalThreads>(cnt, s.tmp, &tot);
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = sel_bm[w];
+    for (int w = wlo; w < whi; ++w) {
+      uint32_t bits = range_bits(sel_bm, w);
       while (bits != 0u) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1u;
