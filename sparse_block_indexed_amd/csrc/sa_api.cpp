@@ -165,16 +165,22 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   // group size guesses how many consecutive tokens share a sequence (any guess
   // is correct, a good one reads each key once).
   a.group_size = std::max(1, std::min(4, n_rows / pd.batch));
-  const int ngroups = (n_rows + a.group_size - 1) / a.group_size;
-  // Few long workgroups: about two per CU (the score kernel's occupancy), so
-  // each workgroup's fixed start-up cost is paid about once per CU.
-  int chunk = 4096;
-  while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < 512) chunk >>= 1;
-  a.chunk_blocks = chunk;
-  a.bitmap_words = a.max_hist_blocks <= sa::kBitmapMaxBlocks ? (a.max_hist_blocks + 31) / 32 : 0;
   // Many query tokens per sequence (a prefill chunk): the score product is a
   // dense GEMM and runs on MFMA; histories must fit the finalize-only select.
   a.use_gemm = n_rows >= 64 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
+  // 16 .. 63 query rows per sequence (verify tokens x per-group queries): one
+  // MFMA pass scores 16 rows against each key, again for fused-select histories.
+  a.use_mfma16 = !a.use_gemm && n_rows >= 16 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
+  const int ngroups = a.use_mfma16 ? (n_rows + 15) / 16 : (n_rows + a.group_size - 1) / a.group_size;
+  // Few long workgroups: about two per CU (the score kernel's occupancy), so
+  // each workgroup's fixed start-up cost is paid about once per CU. The
+  // 16-row MFMA scorer keeps one key tile in flight per wave and fits three
+  // waves per SIMD: it wants about four workgroups per CU.
+  const long long target_wgs = a.use_mfma16 ? 1024 : 512;
+  int chunk = 4096;
+  while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < target_wgs) chunk >>= 1;
+  a.chunk_blocks = chunk;
+  a.bitmap_words = a.max_hist_blocks <= sa::kBitmapMaxBlocks ? (a.max_hist_blocks + 31) / 32 : 0;
   a.key_fp8 = key_fp8;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);

@@ -537,6 +537,133 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
 }
 
 // ---------------------------------------------------------------------------
+// 2c. score with MFMA for 16 query rows of one sequence (e.g. 4 verify tokens
+//     x 4 KV groups with per-group selection), histories of at most kFuseLimit
+// ---------------------------------------------------------------------------
+// A workgroup owns 16 consecutive query rows and a chunk of block ids. Each
+// wave walks a contiguous part of the chunk in tiles of 16 blocks:
+// v_mfma_f32_16x16x32_bf16 with A = the 16 index queries (registers, loaded
+// once) and B = the 16 keys of the tile, loaded straight from the cache into
+// registers (lane (lq, lg): block lq of the tile). k-step i of lane group lg
+// covers dims 64*(i/2) + 16*lg + 8*(i%2) .. +8, so a lane's two k-steps of a
+// 64-dim slice are 16 contiguous dims (32 B of bf16, 16 B of fp8). The next
+// tile's keys are loaded while the current one is multiplied. Rows of another
+// sequence than the one being processed are handled in further passes.
+constexpr int kMfmaRows = 16;
+constexpr int kMfmaTile = 16;
+
+template <bool kFp8>
+__global__ __launch_bounds__(kThreads) void score_mfma_kernel(IndexerArgs a) {
+  constexpr int KB = KeyFmt<kFp8>::kBytes;
+  constexpr int KL = kFp8 ? 4 : 8;   // 16-byte loads per lane per tile
+  __shared__ int32_t s_pages[kMaxChunkBlocks / kBlocksPerPage + 1];
+  __shared__ int s_row_cb[kMfmaRows];
+  __shared__ int s_row_seq[kMfmaRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 15, lg = lane >> 4;
+  const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
+  const int chunk = blockIdx.x % nchunk;
+  const int r0 = (blockIdx.x / nchunk) * kMfmaRows;
+  if (tid < kMfmaRows) {
+    int b = -1, cbt = 0;
+    if (r0 + tid < a.n_tok) cbt = min(hist_blocks(a, r0 + tid, &b), a.max_hist_blocks);
+    s_row_cb[tid] = cbt;
+    s_row_seq[tid] = cbt > 0 ? b : -1;
+  }
+  // A: query row r0 + lq (clamped to the last row; rows past the end store nothing)
+  u32x4 qa[8];
+  {
+    const uint8_t* qrow = a.q_idx + (size_t)min(r0 + lq, a.n_tok - 1) * kKeyBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[i] = load16(qrow + (64 * (i >> 1) + 16 * lg + 8 * (i & 1)) * 2);
+  }
+  __syncthreads();
+  const int lo = chunk * a.chunk_blocks;
+  uint32_t done = 0;
+  for (;;) {
+    int seq = -1, hi = lo;
+    for (int r = 0; r < kMfmaRows; ++r) {
+      if ((done >> r) & 1u) continue;
+      if (s_row_seq[r] < 0 || s_row_cb[r] <= lo) {
+        done |= 1u << r;
+        continue;
+      }
+      if (seq < 0) seq = s_row_seq[r];
+      if (s_row_seq[r] == seq) hi = max(hi, min(s_row_cb[r], lo + a.chunk_blocks));
+    }
+    if (seq < 0) break;
+    uint32_t active = 0;
+    for (int r = 0; r < kMfmaRows; ++r)
+      if (((done >> r) & 1u) == 0 && s_row_seq[r] == seq) active |= 1u << r;
+    done |= active;
+    const int32_t* prow = a.page_table + (size_t)seq * a.max_pages;
+    const int page0 = lo >> 3;
+    const int np = ((hi - 1) >> 3) - page0 + 1;
+    __syncthreads();   // the previous pass is done with s_pages
+    for (int i = tid; i < np; i += kThreads) s_pages[i] = prow[page0 + i];
+    __syncthreads();
+    const int per_wave = ((hi - lo + 4 * kMfmaTile - 1) / (4 * kMfmaTile)) * kMfmaTile;
+    const int wlo = lo + wave * per_wave;
+    const int whi = min(hi, wlo + per_wave);
+    if (wlo < whi) {
+      u32x4 k0[KL], k1[KL];   // two tile buffers (static indices: the loop is unrolled by two)
+      bool ok0 = false, ok1 = false;
+      auto fetch = [&](u32x4 (&kb)[KL], bool& okb, int base) {
+        const int beta = base + lq;
+        const int page = beta < whi ? s_pages[(beta >> 3) - page0] : -1;
+        const bool ok = page >= 0 && page < a.num_pages;
+        okb = ok;
+        const uint8_t* p = a.k_idx_cache + (ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * KB : 0);
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          // bf16: slice j/2 (64 dims = 128 B), half j%2 of the lane's 32 B; fp8: slice j, the lane's 16 B
+          const int off = kFp8 ? 64 * j + 16 * lg : 128 * (j >> 1) + 32 * lg + 16 * (j & 1);
+          kb[j] = load16_stream(p + off);
+        }
+      };
+      const int ntiles = (whi - wlo + kMfmaTile - 1) / kMfmaTile;
+      // rows this lane stores (D: rows 4*lg + r, block lq of the tile)
+      int cb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * lg + r;
+        cb[r] = ((active >> row) & 1u) ? s_row_cb[row] : 0;
+      }
+      // one tile: prefetch tile n + 1 into `nxt`, multiply `cur`, store the scores
+      auto tile = [&](int n, u32x4 (&cur)[KL], bool okc, u32x4 (&nxt)[KL], bool& okn) {
+        const int base = wlo + n * kMfmaTile;
+        if (n + 1 < ntiles) fetch(nxt, okn, base + kMfmaTile);
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          u32x4 b;
+          if constexpr (kFp8) {
+            const u32x4 w = cur[i >> 1];
+            const int h = (i & 1) * 2;
+            b = u32x4{fp8x2_to_bf16x2<false>(w[h]), fp8x2_to_bf16x2<true>(w[h]), fp8x2_to_bf16x2<false>(w[h + 1]),
+                      fp8x2_to_bf16x2<true>(w[h + 1])};
+          } else {
+            b = cur[i];
+          }
+          c = mfma_bf16(qa[i], b, c);
+        }
+        const int beta = base + lq;
+        if (beta < whi) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (beta < cb[r])
+              a.scores[(size_t)(r0 + 4 * lg + r) * a.max_hist_blocks + beta] = okc ? c[r] : -INFINITY;
+        }
+      };
+      fetch(k0, ok0, wlo);
+      for (int n = 0; n < ntiles; n += 2) {
+        tile(n, k0, ok0, k1, ok1);
+        if (n + 1 < ntiles) tile(n + 1, k1, ok1, k0, ok0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. collect
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void collect_kernel(IndexerArgs a) {
@@ -948,6 +1075,15 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
       score_gemm_kernel<true><<<dim3((unsigned)ntt, (unsigned)splits), dim3(kThreads), 0, stream>>>(a, per);
     else
       score_gemm_kernel<false><<<dim3((unsigned)ntt, (unsigned)splits), dim3(kThreads), 0, stream>>>(a, per);
+    finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
+    return hipGetLastError();
+  }
+  if (a.use_mfma16) {   // never with long histories (the host checks)
+    const int nrg = (a.n_tok + kMfmaRows - 1) / kMfmaRows;
+    const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
+    const dim3 grid((unsigned)((long long)nrg * nchunk));
+    if (a.key_fp8) score_mfma_kernel<true><<<grid, dim3(kThreads), 0, stream>>>(a);
+    else score_mfma_kernel<false><<<grid, dim3(kThreads), 0, stream>>>(a);
     finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
     return hipGetLastError();
   }

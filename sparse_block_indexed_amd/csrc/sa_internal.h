@@ -72,6 +72,7 @@ struct IndexerArgs {
   int chunk_blocks;         // blocks per score workgroup
   int bitmap_words;         // LDS bitmap words per finalize workgroup (0: ordered select over all scores)
   bool use_gemm;            // score with the MFMA GEMM kernel (long runs of tokens per sequence)
+  bool use_mfma16;          // score 16 query rows per pass with MFMA (16 .. 63 rows per sequence)
   bool key_fp8;             // index keys are one-byte OCP E4M3 codes (else bf16)
   int32_t* sel_idx;
   uint32_t* hist;           // [n_tok][kHistBins]

@@ -126,3 +126,16 @@ def test_grouped_prefill_gemm_and_long_histories():
         sel, out, lse = _run(wl, qg)
         toks = list(range(0, wl.n_tok, stride))
         _check(wl, qg, sel, out, lse, toks, toks[:6], what=spec.name)
+
+
+def test_grouped_config1_fp8_keys_takes_the_16_row_scorer():
+    """Per-group queries of the 128K workload (16 rows per sequence) with
+    one-byte keys: the 16-row MFMA scorer; selections of 32 tokens."""
+    _say("grouped config 1 fp8 keys")
+    wl = I.config_workload(1, device="cuda")
+    qg = I.grouped_index_queries(wl.n_tok, seed=10, device="cuda")
+    codes = I.fp8_e4m3_codes(wl.k_idx_cache)
+    sel, out, lse = _run(wl, qg, kidx=codes)
+    rng = np.random.default_rng(2)
+    toks = sorted(rng.choice(wl.n_tok, size=32, replace=False).tolist())
+    _check(wl, qg, sel, out, lse, toks, toks[:4], kidx_fp8=codes, what="grouped 128K fp8 keys")

@@ -366,3 +366,34 @@ def test_fp8_index_keys_general_codes():
         torch.cuda.synchronize()
         toks = range(wl.n_tok) if wl.n_tok <= 8 else range(0, wl.n_tok, 7)
         _check_selection(wl, sel, toks, kidx_fp8=codes, what=spec.name)
+
+
+@pytest.mark.parametrize("fp8_keys", [False, True])
+def test_sixteen_row_mfma_scorer_mixed_sequences(fp8_keys):
+    """16 .. 63 query rows per sequence take the 16-row MFMA scorer. With 20
+    verify tokens per sequence its 16-row groups straddle sequences, and short
+    histories (5 and 64 tokens) leave rows with nothing to score."""
+    _say(f"mfma16 mixed fp8={fp8_keys}")
+    from sparse_block_indexed_amd import ops
+    spec = I.WorkloadSpec("m16", batch=5, seq_lens=[5, 64, 1000, 4111, 16000], q_per_seq=20, spare_pages=3)
+    wl = I.make_workload(spec, seed=41, device="cuda")
+    assert wl.n_tok >= 16 * wl.batch           # the 16-row path
+    pt, sl, qs, qp = device_tables(wl)
+    kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if fp8_keys else wl.k_idx_cache
+    sel = ops.indexer_topk(wl.q_idx, kidx, pt, sl, qs, qp, 512)
+    out, lse = ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE)
+    torch.cuda.synchronize()
+    ov = OracleView(wl, kidx_fp8=kidx if fp8_keys else None)
+    sel_h = sel.cpu().numpy()
+    for t in range(wl.n_tok):
+        assert sel_h[t].tolist() == ov.selection(t).tolist(), f"token {t}"
+    toks = list(range(0, wl.n_tok, 7))
+    refs = [ov.sparse(t, sel_h[t]) for t in toks]
+    assert_close_outputs(bf16_to_np(out[toks]), lse[toks].cpu().numpy(), np.stack([r[0] for r in refs]),
+                         np.stack([r[1] for r in refs]), "mfma16")
+    # equal to the per-token scorer's selection (the same call split into 4-token calls)
+    for t0 in range(0, wl.n_tok, 4):
+        t1 = min(wl.n_tok, t0 + 4)
+        part = ops.indexer_topk(wl.q_idx[t0:t1].contiguous(), kidx, pt, sl, qs[t0:t1].contiguous(),
+                                qp[t0:t1].contiguous(), 512)
+        assert torch.equal(part, sel[t0:t1])
