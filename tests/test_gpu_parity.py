@@ -293,6 +293,26 @@ def test_merge_entry_point():
             assert np.abs(lse[t].cpu().numpy() - rl).max() <= 1e-4
 
 
+@pytest.mark.parametrize("heads,dim,S", [(16, 128, 2), (3, 4, 64), (2, 1024, 5), (1024, 8, 1), (64, 192, 33)])
+def test_merge_entry_point_shapes(heads, dim, S):
+    """sa_merge is generic in heads (<= 1024), head dim (multiple of 4, <= 1024)
+    and partitions (<= 64)."""
+    _say(f"merge {heads}x{dim} S={S}")
+    from sparse_block_indexed_amd import ops
+    g = torch.Generator().manual_seed(heads * 7 + dim + S)
+    n_tok = 3
+    po = torch.randn(n_tok, S, heads, dim, generator=g)
+    pl = torch.randn(n_tok, S, heads, generator=g) * 4
+    if S > 1:
+        pl[0, ::2] = -float("inf")                 # some empty partitions
+    out, lse = ops.merge(po.cuda(), pl.cuda())
+    torch.cuda.synchronize()
+    for t in range(n_tok):
+        ro, rl = O.merge(po[t].double().numpy(), pl[t].double().numpy())
+        assert np.abs(bf16_to_np(out[t]) - ro).max() <= 2e-2
+        assert np.abs(lse[t].cpu().numpy() - rl).max() <= 1e-4
+
+
 def test_zero_tokens_is_a_no_op():
     from sparse_block_indexed_amd import ops
     spec = I.WorkloadSpec("z", batch=1, seq_lens=[100], q_per_seq=1)
