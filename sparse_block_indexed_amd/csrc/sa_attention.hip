@@ -71,6 +71,22 @@ __device__ __forceinline__ u32x4 load16_kv(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Max / sum of v over lanes l, l^16, l^32, l^48 (the 4 lane groups holding one
+// head): the row-swap instructions hand each lane {v[l], v[l^16]} (then ^32) in
+// one VALU step, without an LDS round trip.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <bool kStream>
 __device__ __forceinline__ u32x2 load8_kv(const uint8_t* p) {
   if constexpr (kStream) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
@@ -278,8 +294,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     float mx = x[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_groups(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float pr[8];
@@ -342,10 +357,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   }
 
   // ---- merge the 4 wave states (fixed order) and write -------------------
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  float e_tot = e_run + __shfl_xor(e_run, 16);
-  e_tot += __shfl_xor(e_tot, 32);
+  const float l_tot = sum_over_groups(l_run);
+  const float e_tot = sum_over_groups(e_run);
   if (wave > 0) {
 #pragma unroll
     for (int i = 0; i < 12; ++i) s_o[wave - 1][i][lane] = acc[i];
