@@ -8,21 +8,29 @@
 // 8-token block, top 512 blocks) and "What sparse attention does and doesn't
 // save" (the scan over every block key is the read that grows with context).
 //
-// Pipeline (four launches on the caller's stream):
-//  1. zero      clear the per-token histograms and candidate counters.
-//  2. score     stream every historical index key of a sequence once and score
-//               all of that sequence's query tokens against it (v_dot2 bf16 ->
-//               fp32, eight lanes per key, DPP reduction; one-byte E4M3 keys
-//               are widened to bf16 first); write fp32 scores
-//               and add each score to a 2048-bin histogram of the top 11 bits
-//               of its order-preserving key.
-//  3. collect   per (token, score chunk): find the histogram bin that holds the
-//               k-th largest score and append every score at or above that bin
-//               to a small per-token candidate list.
-//  4. finalize  per token: exact radix select (11 + 11 + 10 bits) of the k-th
-//               largest key among the candidates, ties at that key go to the
-//               lower block id, then rank the chosen ids to write them ascending.
-//               A token whose candidate list overflowed takes the same radix
+// Pipeline (launches on the caller's stream; a query row is a token, or a
+// (token, KV group) with per-group selection):
+//  1. zero      (histories over kFuseLimit blocks only) clear the per-row
+//               histograms and candidate counters.
+//  2. score     stream every historical index key of a sequence once per pass
+//               and write fp32 scores. Three scorers, by query rows per
+//               sequence: up to 4 rows share a pass of the per-token scorer
+//               (v_dot2 bf16 -> fp32, eight lanes per key, DPP reduction);
+//               16 .. 63 rows take the 16-row MFMA scorer; 64 and more (a
+//               prefill chunk) the MFMA GEMM. One-byte E4M3 keys are widened
+//               to bf16 on the way in. For long histories the per-token scorer
+//               also adds each score to a 2048-bin histogram of the top 11
+//               bits of its order-preserving key.
+//  3. collect   (long histories only) per (row, score chunk): find the
+//               histogram bin that holds the k-th largest score and append
+//               every score at or above that bin to a per-row candidate list.
+//  4. finalize  per row: histogram of the top 11 key bits (built here from
+//               register-held scores for short histories), everything above the
+//               threshold bin is chosen; within the threshold bin the needed
+//               keys are taken by rank (larger key, then lower block id) or, for
+//               large bins, by two more radix levels and a tie walk in block
+//               order; the chosen ids are written ascending from a bitmap. A row
+//               whose threshold bin or candidate list overflows takes an ordered
 //               select over all of its scores instead.
 
 #include <algorithm>
@@ -140,26 +148,6 @@ __device__ void select_bin(const uint32_t* h, int nbins, uint32_t k, uint32_t* s
     }
   }
   __syncthreads();
-}
-
-// In-place bitonic sort of n (a power of two) values in LDS, by the NT threads.
-template <int NT, typename T, bool kDescending>
-__device__ void bitonic_sort(T* x, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n >> 1); i += NT) {
-        const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));   // stride is a power of two
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0) != kDescending;   // this pair sorts ascending
-        const T a = x[lo], b = x[hi];
-        if ((a > b) == up) {
-          x[lo] = b;
-          x[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
