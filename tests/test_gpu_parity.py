@@ -417,3 +417,23 @@ def test_sixteen_row_mfma_scorer_mixed_sequences(fp8_keys):
         part = ops.indexer_topk(wl.q_idx[t0:t1].contiguous(), kidx, pt, sl, qs[t0:t1].contiguous(),
                                 qp[t0:t1].contiguous(), 512)
         assert torch.equal(part, sel[t0:t1])
+
+
+def test_history_limits_of_the_select_paths():
+    """Around the select paths' size limits, every selection checked against
+    the oracle: a call whose longest history is exactly 16,384 blocks (scores
+    held and selected by finalize alone), the same sequences plus one 8 tokens
+    longer (histograms, collect and candidates), and a context just past 2^17
+    blocks (no room for the LDS bitmaps: the ordered select over all scores)."""
+    from sparse_block_indexed_amd import ops
+    cases = [("fused limit", [131072, 70000], 2),
+             ("collect path", [131072, 131080, 70000], 2),
+             ("past the bitmap limit", [1048576 + 64], 1)]
+    for name, lens, q in cases:
+        _say(f"limits: {name}")
+        wl = I.make_workload(I.WorkloadSpec(name, batch=len(lens), seq_lens=lens, q_per_seq=q), seed=51,
+                             device="cuda")
+        sel, out, lse = run_sparse_layer(wl)
+        _check_all(wl, sel, out, lse, range(wl.n_tok), what=name)
+        del wl, sel, out, lse
+        torch.cuda.empty_cache()
