@@ -13,6 +13,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kMaxPagesPerSeq = 1 << 20;   // positions stay below 2^26
 constexpr int kMaxPoolPages = 1 << 25;     // (page * 4 + group) * 8 + block fits in int32
 constexpr int kMaxGroupedTokens = (1 << 29) - 1;   // tokens x 4 query rows fit in int32
+constexpr long long kMaxGridThreads = 1LL << 32;    // threads of one grid dimension stay below this
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -46,6 +47,10 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   if (!isfinite(softmax_scale)) return SA_ERR_INVALID_ARG;
   if (num_splits > SA_MAX_SPLITS) return SA_ERR_UNSUPPORTED;
   const int S = sa_resolve_num_splits(n_tok, max_blocks, num_splits);
+  // launch limits: fewer than 2^32 threads per grid (attention: 256 per
+  // (token, group, partition); merge: 64 per (token, head))
+  if ((long long)n_tok * sa::kGroups * S * 256 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;
+  if (S > 1 && (long long)n_tok * sa::kHeads * 64 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;
   if (S == 1 && out == nullptr) return SA_ERR_INVALID_ARG;
   if (S > 1 && (part_o == nullptr || part_lse == nullptr)) return SA_ERR_INVALID_ARG;
   if (out != nullptr && !aligned(out, 16)) return SA_ERR_INVALID_ARG;
@@ -136,6 +141,7 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   if (per_group && n_tok > kMaxGroupedTokens) return SA_ERR_UNSUPPORTED;
   // one query row per token, or one per (token, KV group)
   const int n_rows = per_group ? n_tok * sa::kGroups : n_tok;
+  if ((long long)n_rows * 512 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;   // one 512-thread select per row
   if (q_idx == nullptr || k_idx_cache == nullptr || sel_idx == nullptr || workspace == nullptr)
     return SA_ERR_INVALID_ARG;
   if (!aligned(q_idx, 16) || !aligned(k_idx_cache, 16) || !aligned(sel_idx, 4) || !aligned(workspace, 256))
@@ -180,6 +186,11 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   int chunk = 4096;
   while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < target_wgs) chunk >>= 1;
   a.chunk_blocks = chunk;
+  // launch limits of the score and collect grids (256 threads per workgroup)
+  if ((long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) * 256 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;
+  if (a.max_hist_blocks > sa::kFuseLimit &&
+      (long long)n_rows * ((a.max_hist_blocks + sa::kCollectChunk - 1) / sa::kCollectChunk) * 256 >= kMaxGridThreads)
+    return SA_ERR_UNSUPPORTED;
   a.bitmap_words = a.max_hist_blocks <= sa::kBitmapMaxBlocks ? (a.max_hist_blocks + 31) / 32 : 0;
   a.key_fp8 = key_fp8;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -291,6 +302,7 @@ sa_status sa_merge(const float* part_o, const float* part_lse, int n_tok, int nu
     return SA_ERR_UNSUPPORTED;
   if (!aligned(part_o, 16) || !aligned(part_lse, 4) || !aligned(out, 8)) return SA_ERR_INVALID_ARG;
   if (out_lse != nullptr && !aligned(out_lse, 4)) return SA_ERR_INVALID_ARG;
+  if ((long long)n_tok * num_heads * 64 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;   // a wave per (token, head)
   if (sa::launch_merge(part_o, part_lse, n_tok, num_splits, num_heads, head_dim, static_cast<uint16_t*>(out),
                        out_lse, stream) != hipSuccess)
     return SA_ERR_HIP;

@@ -210,6 +210,22 @@ def test_grouped_entry_points_validation(lib):
     assert call(out=None) == ops.SA_ERR_INVALID_ARG
 
 
+def test_grid_limits_are_refused(lib):
+    """Calls whose grids would reach 2^32 threads are refused before any launch."""
+    from sparse_block_indexed_amd import ops
+    d = _desc(ops)
+    huge_ws = ctypes.c_size_t(1 << 62)
+    assert lib.sa_indexer_topk(P, P, d, P, P, 1 << 23, 512, P, P, huge_ws, None) == ops.SA_ERR_UNSUPPORTED
+    long_d = _desc(ops, max_pages=1 << 20, num_pages=1 << 20)                  # 8M-block histories
+    assert lib.sa_indexer_topk(P, P, long_d, P, P, 1 << 16, 512, P, P, huge_ws, None) == ops.SA_ERR_UNSUPPORTED
+    f = lib.sa_sparse_decode
+    assert f(P, P, P, d, P, P, P, 1 << 22, 512, ctypes.c_float(0.1), 1, None, None, P, None, None) \
+        == ops.SA_ERR_UNSUPPORTED                                               # 2^22 tokens x 4 groups x 256
+    assert f(P, P, P, d, P, P, P, 1 << 20, 512, ctypes.c_float(0.1), 2, P, P, P, None, None) \
+        == ops.SA_ERR_UNSUPPORTED                                               # the merge: 2^20 x 64 heads x 64
+    assert lib.sa_merge(P, P, 1 << 20, 2, 64, 192, P, None, None) == ops.SA_ERR_UNSUPPORTED
+
+
 def test_swa_and_merge_validation(lib):
     from sparse_block_indexed_amd import ops
     d = _desc(ops)
