@@ -212,11 +212,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 
   // Loads are branch-free so that the compiler's waits stay precise: a slot
   // with nothing to read (padding, unreadable page) reads unit 0 instead, and
-  // its scores are masked to -inf and its V zeroed below.
-  auto load_k = [&](int c) {
+  // its scores are masked to -inf and its V zeroed below. An `idle` load (the
+  // prefetch after a wave's last chunk) sends every lane to the cache's first
+  // bytes: one line per instruction instead of the whole chunk again.
+  auto load_k = [&](int c, bool idle) {
     const int slot = 4 * c + (lq >> 2);
     const int unit = slot < n ? max(s_unit[slot], 0) : 0;
-    const uint8_t* pk = kbase + (size_t)unit * kUnit;
+    const uint8_t* pk = idle ? a.k_cache : kbase + (size_t)unit * kUnit;
     if constexpr (kFp8) {
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
@@ -232,10 +234,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       }
     }
   };
-  auto load_v = [&](int c) {
+  auto load_v = [&](int c, bool idle) {
     const int slot = 4 * c + lg;
     const int unit = slot < n ? max(s_unit[slot], 0) : 0;
-    const uint8_t* pv = vbase + (size_t)unit * kUnit;
+    const uint8_t* pv = idle ? a.v_cache : vbase + (size_t)unit * kUnit;
     if constexpr (kFp8) {
 #pragma unroll
       for (int i = 0; i < 12; ++i) vq[i] = load8_kv<kStream>(pv + i * 128);
@@ -247,15 +249,16 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 
   // Chunks of this wave: wave, wave + 4, ... The next chunk's K is issued
   // right after the score MFMAs and its V right after the PV MFMAs. The
-  // prefetch is unconditional (the last chunk re-reads itself, an L2 hit) so
+  // prefetch is unconditional (after the last chunk it is an idle load) so
   // that every wait in the loop covers exactly the data it needs.
   int c = wave;
   if (c < nchunks) {
     const int c_last = c + ((nchunks - 1 - c) / kWaves) * kWaves;
-    load_k(c);
-    load_v(c);
+    load_k(c, false);
+    load_v(c, false);
     for (;; c += kWaves) {
     const int cn = min(c + kWaves, c_last);
+    const bool idle = c == c_last;   // nothing left to prefetch
     f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     // keep the refill below the MFMAs that read the K registers: hoisting it
     // would need a second set of them
     __builtin_amdgcn_sched_barrier(0);
-    load_k(cn);
+    load_k(cn, idle);
 
     // this lane's block (lg) of the chunk and its valid positions
     const int slot = 4 * c + lg;
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       for (int i = 0; i < 12; ++i) acc[i] = mfma_bf16(vr[i], pb, acc[i]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_v(cn);
+    load_v(cn, idle);
     if (c == c_last) break;
     }
   }
