@@ -31,6 +31,8 @@
 // land in exactly the lanes the PV step needs them in (half s, row 4*j + r <->
 // block j, token 4*s + r).
 
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -45,6 +47,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSlots = SA_MAX_TOPK + 1 > SA_MAX_WINDOW / 8 + 2 ? SA_MAX_TOPK + 1 : SA_MAX_WINDOW / 8 + 2;
+constexpr int kFillSlots = (kMaxSlots + kThreads - 1) / kThreads * kThreads;   // slot-table rows, whole passes
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 of differences never sees inf-inf
 
@@ -109,12 +112,12 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 template <bool kWindow, bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   constexpr int kUnit = kFp8 ? kUnitBytes / 2 : kUnitBytes;
-  __shared__ int32_t s_unit[kMaxSlots];
-  __shared__ int32_t s_beta[kMaxSlots];
+  __shared__ int32_t s_unit[kFillSlots];   // entries past the token's list are written and never read
+  __shared__ int32_t s_beta[kFillSlots];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_e[kWaves][16];
-  __shared__ f32x4 s_o[kWaves - 1][12][64];
+  __shared__ f32x4 s_o[kWaves][9][64];   // per wave: the 9 output tiles other waves finish
 
   // Split-major order: the workgroups resident at one time share a partition
   // index, i.e. one slice of every token's (ascending) block list, which keeps
@@ -133,13 +136,27 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   const int lg = lane >> 4;
 
   // ---- token and its attended block list --------------------------------
+  // Q, the block ids and the page ids are located from the token's sequence
+  // and position alone (every such read stays inside its table); the sequence
+  // length only decides whether the token is valid, so no load waits for it.
   const int b = a.q_seq[t];
   const int p = a.q_pos[t];
-  bool valid = b >= 0 && b < a.batch && p >= 0;
-  if (valid) valid = p < a.seq_lens[b] && p < a.max_pages * kPageTokens;
-  const int cb = valid ? (p >> 3) : 0;
+  const bool in_range = b >= 0 && b < a.batch && p >= 0 && p < a.max_pages * kPageTokens;
+  const int seq_len = a.seq_lens[in_range ? b : 0];
+
+  // Q of head 16g + lq (B operand of the score MFMA): k-step i of lane group lg
+  // covers dims 64*(i/2) + 16*lg + 8*(i%2) .. +8 (the order of the one-byte K
+  // layout; both cache forms sum in this order)
+  u32x4 qv[6];
+  {
+    const uint8_t* qrow = a.q + ((size_t)t * kHeads + g * kHeadsPerGroup + lq) * (kHeadDim * 2);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) qv[i] = load16(qrow + (64 * (i >> 1) + 16 * lg + 8 * (i & 1)) * 2);
+  }
+
+  const int cb = in_range ? (p >> 3) : 0;
   int nslots = 0, lo = 0, b_lo = 0, nsel = 0;
-  if (valid) {
+  if (in_range) {
     if (kWindow) {
       lo = max(0, p - a.window + 1);
       b_lo = lo >> 3;
@@ -149,45 +166,48 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       nslots = nsel + 1;
     }
   }
-  const int s0 = (int)(((long long)sp * nslots) / S);
-  const int s1 = (int)(((long long)(sp + 1) * nslots) / S);
-  const int n = s1 - s0;
+  // sp * nslots < 64 * 514: 32-bit division
+  const int s0 = (int)((unsigned)(sp * nslots) / (unsigned)S);
+  const int s1 = (int)((unsigned)((sp + 1) * nslots) / (unsigned)S);
+  const int n_all = s1 - s0;
 
-  for (int i = tid; i < n; i += kThreads) {
-    const int slot = s0 + i;
-    int beta;
-    bool ok = true;
-    if (kWindow) {
-      beta = b_lo + slot;
-    } else if (slot < nsel) {
-      beta = a.sel_idx[((size_t)t * (a.sel_per_group ? kGroups : 1) + (a.sel_per_group ? g : 0)) * a.topk + slot];
-      ok = beta >= 0 && beta < cb;
-    } else {
-      beta = cb;
+  // Slot table: every thread issues all of its block-id loads, then all of its
+  // page-id loads; each read is clamped into its table (entries past the list
+  // are read and dropped), so neither waits behind the other's round trip.
+  {
+    constexpr int kFill = kFillSlots / kThreads;
+    const int32_t* prow = a.page_table + (size_t)(in_range ? b : 0) * a.max_pages;
+    const int32_t* srow =
+        a.sel_idx + ((size_t)t * (a.sel_per_group ? kGroups : 1) + (a.sel_per_group ? g : 0)) * a.topk;
+    int beta[kFill];
+    bool ok[kFill];
+#pragma unroll
+    for (int r = 0; r < kFill; ++r) {
+      const int slot = s0 + tid + r * kThreads;
+      if (kWindow) {
+        beta[r] = b_lo + slot;
+        ok[r] = true;
+      } else {
+        const int v = srow[min(slot, a.topk - 1)];
+        beta[r] = slot < nsel ? v : cb;
+        ok[r] = (slot >= nsel) | ((v >= 0) & (v < cb));
+      }
     }
-    int unit = -1;
-    if (ok) {
-      const int page = a.page_table[(size_t)b * a.max_pages + (beta >> 3)];
-      if (page >= 0 && page < a.num_pages)
-        unit = (page * kGroups + g) * kBlocksPerPage + (beta & 7);
+    int page[kFill];
+#pragma unroll
+    for (int r = 0; r < kFill; ++r) page[r] = prow[min(max(beta[r], 0) >> 3, a.max_pages - 1)];
+#pragma unroll
+    for (int r = 0; r < kFill; ++r) {   // unconditional, so that no load is moved behind a branch
+      const bool readable = ok[r] & (page[r] >= 0) & (page[r] < a.num_pages);   // no short circuit: no branch
+      s_unit[tid + r * kThreads] = readable ? (page[r] * kGroups + g) * kBlocksPerPage + (beta[r] & 7) : -1;
+      s_beta[tid + r * kThreads] = ok[r] ? beta[r] : 0;
     }
-    s_unit[i] = unit;
-    s_beta[i] = ok ? beta : 0;
   }
+  const bool valid = in_range && p < seq_len;
+  const int n = valid ? n_all : 0;   // an invalid token attends nothing
   __syncthreads();
 
   // ---- per-wave streaming loop -------------------------------------------
-  // Q of head 16g + lq (B operand of the score MFMA): k-step i of lane group lg covers dims 64*(i/2) + 16*lg + 8*(i%2) .. +8 (the
-  // order of the one-byte K layout; both cache forms sum in this order)
-  u32x4 qv[6];
-  {
-    const uint8_t* qrow = a.q + ((size_t)t * kHeads + g * kHeadsPerGroup + lq) * (kHeadDim * 2);
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int dim0 = 64 * (i >> 1) + 16 * lg + 8 * (i & 1);
-      qv[i] = valid ? load16(qrow + dim0 * 2) : u32x4{0, 0, 0, 0};
-    }
-  }
   const float sc = a.scale_log2;
   const int nchunks = (n + 3) >> 2;
   float m_run = kNegBig;
@@ -212,13 +232,11 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 
   // Loads are branch-free so that the compiler's waits stay precise: a slot
   // with nothing to read (padding, unreadable page) reads unit 0 instead, and
-  // its scores are masked to -inf and its V zeroed below. An `idle` load (the
-  // prefetch after a wave's last chunk) sends every lane to the cache's first
-  // bytes: one line per instruction instead of the whole chunk again.
-  auto load_k = [&](int c, bool idle) {
+  // its scores are masked to -inf and its V zeroed below.
+  auto load_k = [&](int c) {
     const int slot = 4 * c + (lq >> 2);
     const int unit = slot < n ? max(s_unit[slot], 0) : 0;
-    const uint8_t* pk = idle ? a.k_cache : kbase + (size_t)unit * kUnit;
+    const uint8_t* pk = kbase + (size_t)unit * kUnit;
     if constexpr (kFp8) {
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
@@ -234,10 +252,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       }
     }
   };
-  auto load_v = [&](int c, bool idle) {
+  auto load_v = [&](int c) {
     const int slot = 4 * c + lg;
     const int unit = slot < n ? max(s_unit[slot], 0) : 0;
-    const uint8_t* pv = idle ? a.v_cache : vbase + (size_t)unit * kUnit;
+    const uint8_t* pv = vbase + (size_t)unit * kUnit;
     if constexpr (kFp8) {
 #pragma unroll
       for (int i = 0; i < 12; ++i) vq[i] = load8_kv<kStream>(pv + i * 128);
@@ -248,17 +266,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   };
 
   // Chunks of this wave: wave, wave + 4, ... The next chunk's K is issued
-  // right after the score MFMAs and its V right after the PV MFMAs. The
-  // prefetch is unconditional (after the last chunk it is an idle load) so
-  // that every wait in the loop covers exactly the data it needs.
-  int c = wave;
-  if (c < nchunks) {
-    const int c_last = c + ((nchunks - 1 - c) / kWaves) * kWaves;
-    load_k(c, false);
-    load_v(c, false);
-    for (;; c += kWaves) {
-    const int cn = min(c + kWaves, c_last);
-    const bool idle = c == c_last;   // nothing left to prefetch
+  // right after the score MFMAs and its V right after the PV MFMAs. The last
+  // chunk is a separate copy of the body without the prefetch, so that every
+  // wait covers exactly the data it needs and no load is left in flight at the
+  // merge.
+  auto chunk = [&](int c, auto prefetch) {
+    constexpr bool kPrefetch = decltype(prefetch)::value;
+    const int cn = c + kWaves;
     f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
@@ -275,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     // keep the refill below the MFMAs that read the K registers: hoisting it
     // would need a second set of them
     __builtin_amdgcn_sched_barrier(0);
-    load_k(cn, idle);
+    if constexpr (kPrefetch) load_k(cn);
 
     // this lane's block (lg) of the chunk and its valid positions
     const int slot = 4 * c + lg;
@@ -354,17 +368,34 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       for (int i = 0; i < 12; ++i) acc[i] = mfma_bf16(vr[i], pb, acc[i]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_v(cn, idle);
-    if (c == c_last) break;
+    if constexpr (kPrefetch) load_v(cn);
+  };
+  if (wave < nchunks) {
+    const int c_last = wave + ((nchunks - 1 - wave) / kWaves) * kWaves;
+    load_k(wave);
+    load_v(wave);
+    // (a do-while: the V refill at the end of each pass is consumed on every
+    // path, by the next pass or by the last chunk, so it stays where it is)
+    if (wave < c_last) {
+      int c = wave;
+      do {
+        chunk(c, std::true_type{});
+        c += kWaves;
+      } while (c < c_last);
     }
+    chunk(c_last, std::false_type{});
   }
 
   // ---- merge the 4 wave states (fixed order) and write -------------------
+  // Wave w finishes output tiles 3w .. 3w+2: every wave leaves in LDS the 9
+  // tiles the other waves finish, then reads the 3 partial tiles it needs from
+  // each of them (all reads in flight together).
   const float l_tot = sum_over_groups(l_run);
   const float e_tot = sum_over_groups(e_run);
-  if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < 12; ++i) s_o[wave - 1][i][lane] = acc[i];
+  for (int i = 0; i < 12; ++i) {
+    const int owner = i / 3;
+    if (owner != wave) s_o[wave][i - (owner > wave ? 3 : 0)][lane] = acc[i];
   }
   if (lg == 0) {
     s_m[wave][lq] = m_run;
@@ -372,23 +403,34 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     s_e[wave][lq] = e_tot;
   }
   __syncthreads();
-  if (wave != 0) return;
 
-  float M = m_run;
+  float mw[kWaves];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][lq]);
-  const float a0 = __builtin_amdgcn_exp2f(m_run - M);
-  float L = l_tot * a0;
-  float E = e_tot * a0;
+  for (int w = 0; w < kWaves; ++w) mw[w] = s_m[w][lq];
+  // x[w][j]: wave w's partial of tile 3*wave + j (for w == wave a stand-in
+  // read, replaced by the registers)
+  f32x4 x[kWaves][3];
 #pragma unroll
-  for (int i = 0; i < 12; ++i) acc[i] *= a0;
+  for (int w = 0; w < kWaves; ++w) {
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
-    const float aw = __builtin_amdgcn_exp2f(s_m[w][lq] - M);
+    for (int j = 0; j < 3; ++j) x[w][j] = s_o[w][min(3 * wave + j - (wave > w ? 3 : 0), 8)][lane];
+  }
+  f32x4 own[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    own[j] = wave == 0 ? acc[j] : wave == 1 ? acc[3 + j] : wave == 2 ? acc[6 + j] : acc[9 + j];
+  float M = mw[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+  float L = 0.f, E = 0.f;
+  f32x4 o[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float aw = __builtin_amdgcn_exp2f(mw[w] - M);
     L += s_l[w][lq] * aw;
     E += s_e[w][lq] * aw;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) acc[i] += s_o[w - 1][i][lane] * aw;
+    for (int j = 0; j < 3; ++j) o[j] += (w == wave ? own[j] : x[w][j]) * aw;
   }
   const bool any = L > 0.f;
   const float inv = any ? a.v_scale / L : 0.f;   // V scale of a one-byte cache (1 for bf16)
@@ -396,20 +438,20 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   const int head = g * kHeadsPerGroup + lq;
 
   if (S == 1) {
-    uint16_t* orow = a.out + ((size_t)t * kHeads + head) * kHeadDim + 4 * lg;
+    uint16_t* orow = a.out + ((size_t)t * kHeads + head) * kHeadDim + 4 * lg + 48 * wave;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int j = 0; j < 3; ++j) {
       uint2 v;
-      v.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
-      v.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * i) = v;
+      v.x = pack_bf16x2(o[j][0] * inv, o[j][1] * inv);
+      v.y = pack_bf16x2(o[j][2] * inv, o[j][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * j) = v;
     }
-    if (a.out_lse != nullptr && lg == 0) a.out_lse[(size_t)t * kHeads + head] = lse;
+    if (a.out_lse != nullptr && wave == 0 && lg == 0) a.out_lse[(size_t)t * kHeads + head] = lse;
   } else {
-    float* orow = a.part_o + (((size_t)t * S + sp) * kHeads + head) * kHeadDim + 4 * lg;
+    float* orow = a.part_o + (((size_t)t * S + sp) * kHeads + head) * kHeadDim + 4 * lg + 48 * wave;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = acc[i] * inv;
-    if (lg == 0) a.part_lse[((size_t)t * S + sp) * kHeads + head] = lse;
+    for (int j = 0; j < 3; ++j) *reinterpret_cast<f32x4*>(orow + 16 * j) = o[j] * inv;
+    if (wave == 0 && lg == 0) a.part_lse[((size_t)t * S + sp) * kHeads + head] = lse;
   }
 }
 

@@ -46,6 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = 4;
 constexpr int kMaxChunkBlocks = 4096;   // the host never picks a larger score chunk
+constexpr int kPagePasses = (kMaxChunkBlocks / kBlocksPerPage + 1 + kThreads - 1) / kThreads;   // page-id reads per thread
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 // index keys are read once per call
@@ -65,15 +66,34 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Historical block count of query row t (0 for a token whose sequence or
-// position is out of range).
-__device__ __forceinline__ int hist_blocks(const IndexerArgs& a, int t, int* seq_out) {
+// Historical block count of query row t as located from its sequence and
+// position alone (0 when either is out of range): every read it leads to stays
+// inside its table. token_valid() adds the sequence-length check, which decides
+// validity only, so kernels issue their reads first and consume it later.
+__device__ __forceinline__ int located_blocks(const IndexerArgs& a, int t, int* seq_out, int* pos_out) {
   const int b = a.q_seq[t >> a.q_shift];
   const int p = a.q_pos[t >> a.q_shift];
   *seq_out = b;
-  if (b < 0 || b >= a.batch || p < 0) return 0;
-  if (p >= a.seq_lens[b] || p >= a.max_pages * kPageTokens) return 0;
-  return p >> 3;
+  *pos_out = p;
+  // no short circuit: both reads are issued together
+  return (b >= 0) & (b < a.batch) & (p >= 0) & (p < a.max_pages * kPageTokens) ? p >> 3 : 0;
+}
+
+// The length of sequence b, read without a branch (b clamped; batch >= 1), so
+// that the read is issued at once and waited for only where it is used.
+__device__ __forceinline__ int seq_len_of(const IndexerArgs& a, int b) {
+  return a.seq_lens[min(max(b, 0), a.batch - 1)];
+}
+
+__device__ __forceinline__ bool token_valid(const IndexerArgs& a, int b, int p, int len) {
+  return (b >= 0) & (b < a.batch) & (p >= 0) & (p < a.max_pages * kPageTokens) & (p < len);
+}
+
+// Historical block count of query row t (0 for an invalid token).
+__device__ __forceinline__ int hist_blocks(const IndexerArgs& a, int t, int* seq_out) {
+  int p;
+  const int n = located_blocks(a, t, seq_out, &p);
+  return token_valid(a, *seq_out, p, seq_len_of(a, *seq_out)) ? n : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -307,21 +327,27 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
 // register sets.
 // With kHist the kernel also builds each token's 2048-bin histogram of score
 // keys (needed when the history is too long for finalize to hold all scores).
+static_assert(kMaxGroup == 4 && kMaxGroup * (kKeyBytes / 16) <= kThreads, "one index-query load per thread");
+
 template <int GS, bool kHist, bool kFp8>
 __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
   __shared__ uint32_t s_hist[kHist ? GS : 1][kHistBins];
-  __shared__ int32_t s_pages[kMaxChunkBlocks / kBlocksPerPage + 1];
-  __shared__ u32x4 s_q[GS * (kKeyBytes / 16)];   // index queries of the current run
+  __shared__ int32_t s_pages[kPagePasses * kThreads];   // page ids of the current run's blocks (padded)
+  __shared__ u32x4 s_q[kThreads];   // index queries of the current run (padded)
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const int chunk = blockIdx.x % nchunk;
   const int grp = blockIdx.x / nchunk;
   const int t0 = grp * GS;
   const int ng = min(GS, a.n_tok - t0);
+  // Rows are located without the sequence-length check: a row past its
+  // sequence's length is scored all the same (its scores and histogram are
+  // never used), and no read waits for that check.
   int seq[kMaxGroup], ncb[kMaxGroup];
   for (int j = 0; j < kMaxGroup; ++j) {
     ncb[j] = 0;
     seq[j] = -1;
-    if (j < ng) ncb[j] = min(hist_blocks(a, t0 + j, &seq[j]), a.max_hist_blocks);
+    int pj;
+    if (j < ng) ncb[j] = min(located_blocks(a, t0 + j, &seq[j], &pj), a.max_hist_blocks);
   }
   const int lo = chunk * a.chunk_blocks;
   bool any = false;
@@ -336,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
   uint32_t done = 0;
   for (int j0 = 0; j0 < ng; ++j0) {
     if ((done >> j0) & 1u) continue;
-    int tok[kMaxGroup], hslot[kMaxGroup], cbs[kMaxGroup];
+    int tok[kMaxGroup] = {t0, t0, t0, t0}, hslot[kMaxGroup], cbs[kMaxGroup];
     int nq = 0, hi = lo;
     for (int j = j0; j < ng; ++j) {
       if (((done >> j) & 1u) == 0 && seq[j] == seq[j0]) {
@@ -351,13 +377,21 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
       }
     }
     if (nq == 0) continue;
-    // physical pages of blocks [lo, hi) of this sequence
-    const int32_t* prow = a.page_table + (size_t)seq[j0] * a.max_pages;
+    // Physical pages of blocks [lo, hi) of this sequence and the run's index
+    // queries, read in one pass before the barrier (reads clamped into their
+    // tables, LDS writes unconditional: no read waits behind another).
+    const int32_t* prow = a.page_table + (size_t)seq[j0] * a.max_pages + (lo >> 3);
     const int np = ((hi - 1) >> 3) - (lo >> 3) + 1;
-    __syncthreads();   // the previous run is done with s_pages
-    for (int i = threadIdx.x; i < np; i += kThreads) s_pages[i] = prow[(lo >> 3) + i];
-    for (int i = threadIdx.x; i < nq * (kKeyBytes / 16); i += kThreads)
-      s_q[i] = load16(a.q_idx + (size_t)tok[i / (kKeyBytes / 16)] * kKeyBytes + (i % (kKeyBytes / 16)) * 16);
+    const int qi = min((int)threadIdx.x / (kKeyBytes / 16), nq - 1);
+    const int tq = qi == 0 ? tok[0] : qi == 1 ? tok[1] : qi == 2 ? tok[2] : tok[3];
+    const u32x4 qv = load16(a.q_idx + (size_t)tq * kKeyBytes + (threadIdx.x % (kKeyBytes / 16)) * 16);
+    int pg[kPagePasses];
+#pragma unroll
+    for (int r = 0; r < kPagePasses; ++r) pg[r] = prow[min((int)threadIdx.x + r * kThreads, np - 1)];
+    __syncthreads();   // the previous run is done with s_pages and s_q
+    s_q[threadIdx.x] = qv;
+#pragma unroll
+    for (int r = 0; r < kPagePasses; ++r) s_pages[threadIdx.x + r * kThreads] = pg[r];
     __syncthreads();
     if (nq == 1) score_run<1, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist);
     if constexpr (GS >= 2) { if (nq == 2) score_run<2, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
@@ -551,9 +585,9 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(IndexerArgs a) {
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const int chunk = blockIdx.x % nchunk;
   const int r0 = (blockIdx.x / nchunk) * kMfmaRows;
-  if (tid < kMfmaRows) {
-    int b = -1, cbt = 0;
-    if (r0 + tid < a.n_tok) cbt = min(hist_blocks(a, r0 + tid, &b), a.max_hist_blocks);
+  if (tid < kMfmaRows) {   // rows located as in score_kernel (no sequence-length check)
+    int b = -1, p, cbt = 0;
+    if (r0 + tid < a.n_tok) cbt = min(located_blocks(a, r0 + tid, &b, &p), a.max_hist_blocks);
     s_row_cb[tid] = cbt;
     s_row_seq[tid] = cbt > 0 ? b : -1;
   }
@@ -663,8 +697,9 @@ __global__ __launch_bounds__(kThreads) void collect_kernel(IndexerArgs a) {
   const int nck = (a.max_hist_blocks + kCollectChunk - 1) / kCollectChunk;
   const int ck = blockIdx.x % nck;
   const int t = blockIdx.x / nck;
-  int b;
-  const int ncand = min(hist_blocks(a, t, &b), a.max_hist_blocks);
+  int b, p;
+  const int ncand = min(located_blocks(a, t, &b, &p), a.max_hist_blocks);
+  const int len = seq_len_of(a, b);   // consumed once the loads below are in flight
   const int lo = ck * kCollectChunk;
   if (ncand <= kFuseLimit || lo >= ncand) return;   // short histories select in finalize
   const int hi = min(ncand, lo + kCollectChunk);
@@ -690,7 +725,7 @@ __global__ __launch_bounds__(kThreads) void collect_kernel(IndexerArgs a) {
   }
   uint32_t total;
   const uint32_t off = block_prefix_exclusive<kThreads>(cnt, s_tmp, &total);
-  if (total == 0) return;
+  if (total == 0 || !token_valid(a, b, p, len)) return;   // an invalid token lists nothing
   if (threadIdx.x == 0) s_base = atomicAdd(&a.cand_count[t], total);
   __syncthreads();
   uint32_t pos = s_base + off;
@@ -806,11 +841,15 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   extern __shared__ uint32_t s_bm[];   // [2][bitmap_words]: chosen ids, ids tied at tau
   const int t = blockIdx.x;
   const int k = a.topk;
-  int b;
-  const int ncand = min(hist_blocks(a, t, &b), a.max_hist_blocks);
+  // The scores are located from the token's sequence and position; the
+  // sequence-length check is consumed after their loads are in flight.
+  int b, p;
+  const int ncand = min(located_blocks(a, t, &b, &p), a.max_hist_blocks);
+  const int len = seq_len_of(a, b);
   int32_t* out = a.sel_idx + (size_t)t * k;
   if (ncand <= k) {
-    for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = i < ncand ? i : -1;
+    const int nv = token_valid(a, b, p, len) ? ncand : 0;
+    for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = i < nv ? i : -1;
     return;
   }
   const int nw = (ncand + 31) >> 5;                 // bitmap words this token needs
@@ -857,6 +896,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
       }
     }
     __syncthreads();
+  }
+  if (!token_valid(a, b, p, len)) {   // past its sequence's length: selects nothing
+    for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = -1;
+    return;
   }
   select_bin<kFinalThreads>(s.h, kHistBins, (uint32_t)k, s.tmp, s.res);
   const uint32_t b1 = s.res[0];
