@@ -76,7 +76,7 @@ __device__ __forceinline__ int located_blocks(const IndexerArgs& a, int t, int* 
   *seq_out = b;
   *pos_out = p;
   // no short circuit: both reads are issued together
-  return (b >= 0) & (b < a.batch) & (p >= 0) & (p < a.max_pages * kPageTokens) ? p >> 3 : 0;
+  return ((b >= 0) & (b < a.batch) & (p >= 0) & (p < a.max_pages * kPageTokens)) ? p >> 3 : 0;
 }
 
 // The length of sequence b, read without a branch (b clamped; batch >= 1), so
@@ -97,44 +97,66 @@ __device__ __forceinline__ int hist_blocks(const IndexerArgs& a, int t, int* seq
 }
 
 // ---------------------------------------------------------------------------
-// block-wide helpers (256 threads = 4 waves)
+// wave- and block-wide helpers (NT threads = NT / 64 waves)
 // ---------------------------------------------------------------------------
+
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP moves: shifts by
+// 1, 2, 4 and 8 lanes inside each row of 16, then lane 15 of each row added to
+// the next row and lane 31 to the upper half.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15 (rows 1, 3)
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31 (rows 2, 3)
+  return x;
+}
+
+// Exclusive prefix sum over the lanes of a wave of values below 2^NB, one
+// ballot per bit plane (no cross-lane moves); *total receives the wave's sum.
+template <int NB>
+__device__ __forceinline__ uint32_t wave_excl_scan_small(uint32_t c, uint32_t* total) {
+  uint32_t ex = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const uint64_t m = __ballot((c >> b) & 1u);
+    ex += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    tot += (uint32_t)__popcll(m) << b;
+  }
+  *total = tot;
+  return ex;
+}
 
 // Exclusive suffix sum over the NT threads of the block: the sum of v over
 // threads with a larger index. s_tmp holds NT / 64 words.
 template <int NT>
 __device__ uint32_t block_suffix_exclusive(uint32_t v, uint32_t* s_tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(x, off);
-    if (lane + off < 64) x += y;
-  }
-  if (lane == 0) s_tmp[wave] = x;   // wave total
+  const int wave = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  const uint32_t wave_tot = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  if ((threadIdx.x & 63) == 63) s_tmp[wave] = x;
   __syncthreads();
   uint32_t above = 0;
-  for (int w = wave + 1; w < NT / 64; ++w) above += s_tmp[w];
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) above += w > wave ? s_tmp[w] : 0u;
   __syncthreads();
-  return above + x - v;
+  return above + wave_tot - x;
 }
 
 // Exclusive prefix sum over the NT threads; *total receives the block total.
 template <int NT>
 __device__ uint32_t block_prefix_exclusive(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) s_tmp[wave] = x;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) s_tmp[wave] = x;
   __syncthreads();
   uint32_t below = 0, tot = 0;
+#pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
-    if (w < wave) below += s_tmp[w];
-    tot += s_tmp[w];
+    const uint32_t y = s_tmp[w];
+    below += w < wave ? y : 0u;
+    tot += y;
   }
   __syncthreads();
   *total = tot;
@@ -143,8 +165,9 @@ __device__ uint32_t block_prefix_exclusive(uint32_t v, uint32_t* s_tmp, uint32_t
 
 // Among bins h[0..nbins) (a higher bin holds larger keys), find the bin that
 // holds the k-th largest element: above < k <= above + h[bin], where above is
-// the count in higher bins. Needs sum(h) >= k >= 1 and nbins a multiple of NT.
-// Result is broadcast through s_res[0] (bin) and s_res[1] (above).
+// the count in higher bins. Needs sum(h) >= k >= 1, nbins a multiple of 2 NT
+// and h 16-byte aligned. Result is broadcast through s_res[0] (bin) and
+// s_res[1] (above).
 template <int NT>
 __device__ void select_bin(const uint32_t* h, int nbins, uint32_t k, uint32_t* s_tmp, uint32_t* s_res) {
   if (threadIdx.x == 0) {   // defined result even for inconsistent input
@@ -154,7 +177,17 @@ __device__ void select_bin(const uint32_t* h, int nbins, uint32_t k, uint32_t* s
   const int per = nbins / NT;
   const int b0 = threadIdx.x * per;
   uint32_t part = 0;
-  for (int i = 0; i < per; ++i) part += h[b0 + i];
+  if (per % 4 == 0) {   // 16-byte reads: consecutive lanes read consecutive bytes
+    for (int i = 0; i < per; i += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(h + b0 + i);
+      part += q.x + q.y + q.z + q.w;
+    }
+  } else {
+    for (int i = 0; i < per; i += 2) {
+      const uint2 q = *reinterpret_cast<const uint2*>(h + b0 + i);
+      part += q.x + q.y;
+    }
+  }
   uint32_t cum = block_suffix_exclusive<NT>(part, s_tmp);
   if (cum < k && cum + part >= k) {
     for (int i = per - 1; i >= 0; --i) {
@@ -690,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(IndexerArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void collect_kernel(IndexerArgs a) {
   constexpr int kPer = kCollectChunk / kThreads;
-  __shared__ uint32_t s_h[kHistBins];
+  __shared__ __align__(16) uint32_t s_h[kHistBins];
   __shared__ uint32_t s_tmp[4];
   __shared__ uint32_t s_res[2];
   __shared__ uint32_t s_base;
@@ -752,10 +785,92 @@ __device__ __forceinline__ uint64_t tz_entry(uint32_t key, uint32_t beta) { retu
 __device__ __forceinline__ uint32_t tz_key(uint64_t e) { return (uint32_t)(e >> 32); }
 __device__ __forceinline__ uint32_t tz_block(uint64_t e) { return ~(uint32_t)e; }
 
+// Writes the ids of the bits set in sel_bm, together with the first need_eq
+// ids (in block order) of the bits set in eq_bm, in ascending order to out
+// (at most k; -1 past the last). Thread i owns the contiguous id range
+// [i*perb, (i+1)*perb), perb = ceil(nbits / threads): it reads the (at most
+// kEmitWords) words its range touches all at once, one scan of its packed
+// (chosen, tied) counts gives its offsets (one barrier), and it places its ids
+// -- taking the leading tied ids of its range -- in LDS (s_ids, k entries),
+// which is then written out in one coalesced pass.
+constexpr int kEmitWords = kBitmapMaxBlocks / 32 / kFinalThreads + 1;
+
+__device__ __forceinline__ void emit_selection(const uint32_t* sel_bm, const uint32_t* eq_bm, uint32_t need_eq, int nbits, int k,
+                               int32_t* out, uint32_t* s_tmp, int32_t* s_ids) {
+  constexpr int kW = kFinalThreads / 64;
+  const int wave = threadIdx.x >> 6;
+  const bool use_eq = need_eq > 0u;   // block-uniform
+  const int nw = (nbits + 31) >> 5;
+  const int perb = (nbits + kFinalThreads - 1) / kFinalThreads;
+  const int bb0 = min(nbits, (int)threadIdx.x * perb), bb1 = min(nbits, bb0 + perb);
+  const int wlo = bb0 >> 5;
+  const int nwt = bb1 > bb0 ? ((bb1 - 1) >> 5) - wlo + 1 : 0;   // words this range touches
+  uint32_t sw[kEmitWords], ew[kEmitWords];
+  uint32_t cs = 0, ce = 0;
+#pragma unroll
+  for (int i = 0; i < kEmitWords; ++i) {
+    const int w = wlo + i;
+    const int lo = min(max(bb0 - 32 * w, 0), 31), hi = min(max(bb1 - 32 * w, 0), 32);
+    const uint32_t mask = i < nwt ? (hi >= 32 ? 0xffffffffu : (1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
+    const int wr = min(w, nw - 1);   // clamped read: every read is issued, none waits on another
+    sw[i] = sel_bm[wr] & mask;
+    ew[i] = use_eq ? eq_bm[wr] & mask : 0u;
+    cs += (uint32_t)__popc(sw[i]);
+    ce += (uint32_t)__popc(ew[i]);
+  }
+  // packed scan: chosen ids <= k and tied ids <= the tie capacity, both below 2^16
+  const uint32_t packed = cs | ce << 16;
+  const uint32_t incl = wave_incl_scan(packed);
+  if ((threadIdx.x & 63) == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  uint32_t below = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kW; ++i) {
+    const uint32_t y = s_tmp[i];
+    below += i < wave ? y : 0u;
+    tot += y;
+  }
+  const uint32_t ex = below + incl - packed;
+  uint32_t sbefore = ex & 0xffffu, ebefore = ex >> 16;   // chosen / tied ids in lower ranges
+#pragma unroll
+  for (int i = 0; i < kEmitWords; ++i) {
+    uint32_t take = 0;
+    if (ebefore < need_eq && ew[i] != 0u) {
+      const uint32_t r = need_eq - ebefore;
+      if ((uint32_t)__popc(ew[i]) <= r) {
+        take = ew[i];
+      } else {
+        uint32_t rest = ew[i];
+        for (uint32_t j = 0; j < r; ++j) {
+          const uint32_t low = rest & (0u - rest);
+          take |= low;
+          rest ^= low;
+        }
+      }
+    }
+    uint32_t fin = sw[i] | take;
+    uint32_t pos = sbefore + min(need_eq, ebefore);
+    while (fin != 0u) {
+      const int bit = __ffs(fin) - 1;
+      fin &= fin - 1u;
+      if (pos < (uint32_t)k) s_ids[pos] = (wlo + i) * 32 + bit;
+      ++pos;
+    }
+    sbefore += (uint32_t)__popc(sw[i]);
+    ebefore += (uint32_t)__popc(ew[i]);
+  }
+  __syncthreads();
+  const int n_out = (int)min((uint32_t)k, (tot & 0xffffu) + min(need_eq, tot >> 16));
+  for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = i < n_out ? s_ids[i] : -1;   // -1 only if inconsistent
+}
+
+static_assert(kTieCap * 2 >= SA_MAX_TOPK, "the tie buffer stages the output ids");
+static_assert(SA_MAX_TOPK < (1 << 16) && kTieCap < (1 << 16), "emit_selection packs two counts in 32 bits");
+
 struct alignas(16) FinalizeLds {
   uint64_t tz[kTieCap];     // threshold-bin entries: key << 32 | ~block id (a larger entry ranks first)
   uint32_t h[kHistBins];
-  uint32_t tmp[kFinalThreads / 64];
+  uint32_t tmp[2 * (kFinalThreads / 64)];   // block scans; emit_selection uses both halves
   uint32_t res[2];
   uint32_t n_tz;
 };
@@ -836,40 +951,37 @@ __device__ void select_ordered_global(const IndexerArgs& a, FinalizeLds& s, int 
 // order until k are taken (a bitmap walk). The chosen ids are written ascending
 // by walking the selection bitmap. Short histories read their scores directly,
 // long ones the candidates gathered by collect_kernel.
-__global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) {
-  __shared__ FinalizeLds s;
-  extern __shared__ uint32_t s_bm[];   // [2][bitmap_words]: chosen ids, ids tied at tau
-  const int t = blockIdx.x;
+// Histogram and classification of one token's scores. KP > 0: a history of
+// at most KP * kFinalThreads blocks whose scores are held in registers, KP per
+// thread (instantiated for 2 .. 32 so that short histories execute no steps
+// past their own); KP == 0: a longer history, from the score pass's histogram
+// and the collect pass's candidates. Afterwards sel_bm holds the ids above the
+// threshold bin b1 (*above of them) and s.tz the threshold-bin entries.
+// Returns kClassified, kDone (an invalid token: its output is written) or
+// kFallback (the history does not fit the LDS structures: the caller selects
+// it in order over all scores).
+enum ClassifyResult { kClassified, kDone, kFallback };
+
+template <int KP>
+__device__ __forceinline__ ClassifyResult finalize_classify(const IndexerArgs& a, FinalizeLds& s, uint32_t* sel_bm, uint32_t* eq_bm, int t,
+                                  int ncand, bool valid, int32_t* out, uint32_t* b1_out, uint32_t* above_out) {
+  constexpr bool kFused = KP > 0;
+  constexpr int kPer = kFused ? KP : 1;
+  constexpr int kGroup = kPer < 8 ? kPer : 8;   // steps whose loads are issued together
   const int k = a.topk;
-  // The scores are located from the token's sequence and position; the
-  // sequence-length check is consumed after their loads are in flight.
-  int b, p;
-  const int ncand = min(located_blocks(a, t, &b, &p), a.max_hist_blocks);
-  const int len = seq_len_of(a, b);
-  int32_t* out = a.sel_idx + (size_t)t * k;
-  if (ncand <= k) {
-    const int nv = token_valid(a, b, p, len) ? ncand : 0;
-    for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = i < nv ? i : -1;
-    return;
-  }
-  const int nw = (ncand + 31) >> 5;                 // bitmap words this token needs
-  uint32_t* sel_bm = s_bm;
-  uint32_t* eq_bm = s_bm + a.bitmap_words;
-  const bool fused = ncand <= kFuseLimit;
-  // a short history's scores are held in registers from here on
-  constexpr int kPer = kFuseLimit / kFinalThreads;
+  const int nw = (ncand + 31) >> 5;   // bitmap words this token needs
   const int jmax = (ncand + kFinalThreads - 1) / kFinalThreads;   // steps j that hold scores (uniform)
   uint32_t kv[kPer];
-  if (fused) {
-    // every load of a step is issued (past the history they re-read its last
+  if constexpr (kFused) {
+    // every load of a group is issued (past the history they re-read its last
     // score), so all of them are in flight at once
     const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
     float sv[kPer];
 #pragma unroll
-    for (int j0 = 0; j0 < kPer; j0 += 8) {   // groups of 8 steps, each group's loads unconditional
+    for (int j0 = 0; j0 < kPer; j0 += kGroup) {
       if (j0 < jmax) {
 #pragma unroll
-        for (int j = j0; j < j0 + 8; ++j) sv[j] = srow[min(j * kFinalThreads + (int)threadIdx.x, ncand - 1)];
+        for (int j = j0; j < j0 + kGroup; ++j) sv[j] = srow[min(j * kFinalThreads + (int)threadIdx.x, ncand - 1)];
       }
     }
 #pragma unroll
@@ -887,7 +999,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   }
   if (threadIdx.x == 0) s.n_tz = 0;
   __syncthreads();
-  if (fused) {   // the score pass built no histogram for short histories
+  if constexpr (kFused) {   // the score pass built no histogram for short histories
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       if (j < jmax) {
@@ -897,31 +1009,20 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
     }
     __syncthreads();
   }
-  if (!token_valid(a, b, p, len)) {   // past its sequence's length: selects nothing
+  if (!valid) {   // past its sequence's length: selects nothing
     for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = -1;
-    return;
+    return kDone;
   }
   select_bin<kFinalThreads>(s.h, kHistBins, (uint32_t)k, s.tmp, s.res);
   const uint32_t b1 = s.res[0];
   const uint32_t above = min(s.res[1], (uint32_t)k - 1u);
   const uint32_t in_bin = s.h[b1];
-  const uint32_t n_listed = fused ? 0u : a.cand_count[t];
-  if (nw > a.bitmap_words || in_bin > (uint32_t)kTieCap || (!fused && n_listed > (uint32_t)kCandCap)) {
-    select_ordered_global(a, s, t, ncand, out);
-    return;
-  }
-  auto classify = [&](uint32_t key, uint32_t beta) {
-    const uint32_t bin = key >> 21;
-    if (bin > b1) {
-      atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
-    } else if (bin == b1) {
-      const uint32_t slot = atomicAdd(&s.n_tz, 1u);
-      if (slot < (uint32_t)kTieCap) {
-        s.tz[slot] = tz_entry(key, beta);
-      }
-    }
-  };
-  if (fused) {
+  const uint32_t n_listed = kFused ? 0u : a.cand_count[t];
+  if (nw > a.bitmap_words || in_bin > (uint32_t)kTieCap || (!kFused && n_listed > (uint32_t)kCandCap))
+    return kFallback;
+  *b1_out = b1;
+  *above_out = above;
+  if constexpr (kFused) {
     // A wave holds 64 consecutive block ids per j: its ballot of "above the
     // threshold bin" is exactly two bitmap words, and the threshold-bin keys
     // take one counter update per wave.
@@ -932,12 +1033,12 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       if (j < jmax) {
-        const bool valid = j * kFinalThreads + (int)threadIdx.x < ncand;
+        const bool in = j * kFinalThreads + (int)threadIdx.x < ncand;
         const uint32_t bin = kv[j] >> 21;
-        const uint64_t above_mask = __ballot(valid && bin > b1);
+        const uint64_t above_mask = __ballot(in && bin > b1);
         word_lo = lane == j ? (uint32_t)above_mask : word_lo;
         word_hi = lane == j ? (uint32_t)(above_mask >> 32) : word_hi;
-        n_wave += (uint32_t)__popcll(__ballot(valid && bin == b1));
+        n_wave += (uint32_t)__popcll(__ballot(in && bin == b1));
       }
     }
     if (lane < jmax) {
@@ -967,22 +1068,53 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   } else {
     for (uint32_t i = threadIdx.x; i < n_listed; i += kFinalThreads) {
       const uint2 c = a.cand[(size_t)t * kCandCap + i];
-      classify(c.x, c.y);
+      const uint32_t key = c.x, beta = c.y, bin = key >> 21;
+      if (bin > b1) {
+        atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
+      } else if (bin == b1) {
+        const uint32_t slot = atomicAdd(&s.n_tz, 1u);
+        if (slot < (uint32_t)kTieCap) s.tz[slot] = tz_entry(key, beta);
+      }
     }
   }
   __syncthreads();
+  return kClassified;
+}
+
+__global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) {
+  __shared__ FinalizeLds s;
+  extern __shared__ uint32_t s_bm[];   // [2][bitmap_words]: chosen ids, ids tied at tau
+  const int t = blockIdx.x;
+  const int k = a.topk;
+  // The scores are located from the token's sequence and position; the
+  // sequence-length check is consumed after their loads are in flight.
+  int b, p;
+  const int ncand = min(located_blocks(a, t, &b, &p), a.max_hist_blocks);
+  const int len = seq_len_of(a, b);
+  int32_t* out = a.sel_idx + (size_t)t * k;
+  if (ncand <= k) {
+    const int nv = token_valid(a, b, p, len) ? ncand : 0;
+    for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
+  uint32_t* sel_bm = s_bm;
+  uint32_t* eq_bm = s_bm + a.bitmap_words;
+  const bool valid = token_valid(a, b, p, len);
+  const int jmax = (ncand + kFinalThreads - 1) / kFinalThreads;
+  uint32_t b1 = 0, above = 0;
+  ClassifyResult r;
+  if (ncand > kFuseLimit) r = finalize_classify<0>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
+  else if (jmax <= 2) r = finalize_classify<2>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
+  else if (jmax <= 4) r = finalize_classify<4>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
+  else if (jmax <= 8) r = finalize_classify<8>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
+  else if (jmax <= 16) r = finalize_classify<16>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
+  else r = finalize_classify<32>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
+  static_assert(kFuseLimit == 32 * kFinalThreads, "the largest instantiation covers every fused history");
+  if (r == kFallback) select_ordered_global(a, s, t, ncand, out);
+  if (r != kClassified) return;
   const int m = (int)min(s.n_tz, (uint32_t)kTieCap);
   const uint32_t need = (uint32_t)k - above;
-  // contiguous range of block ids [bb0, bb1) of this thread (so that every
-  // thread has bits to walk even for short histories)
-  const int perb = (ncand + kFinalThreads - 1) / kFinalThreads;
-  const int bb0 = min(ncand, (int)threadIdx.x * perb), bb1 = min(ncand, bb0 + perb);
-  const int wlo = bb0 >> 5, whi = bb1 > bb0 ? ((bb1 - 1) >> 5) + 1 : wlo;
-  auto range_bits = [&](const uint32_t* bm, int w) -> uint32_t {
-    const int lo = max(bb0 - 32 * w, 0), hi = min(bb1 - 32 * w, 32);   // 0 <= lo < hi <= 32
-    const uint32_t mhi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
-    return bm[w] & mhi & ~((1u << lo) - 1u);
-  };
+  uint32_t need_eq = 0;   // ids tied at the exact threshold, taken in block order
   if (m <= kRankMax) {
     // Few keys in the threshold bin: a key is chosen iff fewer than `need` of
     // them come before it (a larger key, or an equal key of a lower block).
@@ -1000,7 +1132,6 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
       const uint32_t beta = tz_block(e);
       if (rank < need) atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
     }
-    __syncthreads();
   } else {
     // exact k-th key inside the threshold bin: two more radix levels
     uint32_t prefix = b1 << 21;
@@ -1026,48 +1157,15 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
       }
     }
     const uint32_t tau = prefix;
-    const uint32_t need_eq = need - min(gt_in_bin, need);
+    need_eq = need - min(gt_in_bin, need);
     for (int i = threadIdx.x; i < m; i += kFinalThreads) {
       const uint32_t key = tz_key(s.tz[i]), beta = tz_block(s.tz[i]);
       if (key > tau) atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
       else if (key == tau) atomicOr(&eq_bm[beta >> 5], 1u << (beta & 31));
     }
-    __syncthreads();
-    // ties at tau: the first need_eq in block order
-    uint32_t cnt = 0;
-    for (int w = wlo; w < whi; ++w) cnt += (uint32_t)__popc(range_bits(eq_bm, w));
-    uint32_t tot;
-    uint32_t before = block_prefix_exclusive<kFinalThreads>(cnt, s.tmp, &tot);
-    for (int w = wlo; w < whi && before < need_eq; ++w) {
-      uint32_t bits = range_bits(eq_bm, w);
-      uint32_t take = 0;
-      while (bits != 0u && before < need_eq) {
-        const uint32_t low = bits & (0u - bits);
-        take |= low;
-        bits ^= low;
-        ++before;
-      }
-      if (take) atomicOr(&sel_bm[w], take);   // a word can straddle two threads' ranges
-    }
-    __syncthreads();
   }
-  // ascending output
-  {
-    uint32_t cnt = 0;
-    for (int w = wlo; w < whi; ++w) cnt += (uint32_t)__popc(range_bits(sel_bm, w));
-    uint32_t tot;
-    uint32_t pos = block_prefix_exclusive<kFinalThreads>(cnt, s.tmp, &tot);
-    for (int w = wlo; w < whi; ++w) {
-      uint32_t bits = range_bits(sel_bm, w);
-      while (bits != 0u) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1u;
-        if (pos < (uint32_t)k) out[pos] = (int32_t)(w * 32 + bit);
-        ++pos;
-      }
-    }
-    for (uint32_t i = tot + threadIdx.x; i < (uint32_t)k; i += kFinalThreads) out[i] = -1;   // only if inconsistent
-  }
+  __syncthreads();   // (the threshold-bin entries are dead from here: their LDS stages the output)
+  emit_selection(sel_bm, eq_bm, need_eq, ncand, k, out, s.tmp, reinterpret_cast<int32_t*>(s.tz));
 }
 
 }  // namespace
