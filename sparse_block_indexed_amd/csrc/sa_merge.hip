@@ -24,16 +24,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // One wave per (token, head). Lane s < S holds partition s's lse and weight
 // e^(lse_s - M); the wave reduces M and the weight sum, then every lane
 // accumulates its 4-dim slices over the partitions in order 0..S-1 with eight
-// loads in flight (the weight of partition s is broadcast from lane s).
+// loads in flight (the weight of partition s is broadcast from lane s). The
+// first eight partitions' slices are read before the lse values: neither read
+// waits for the other.
+// Reductions over the 64 lanes as butterflies (DPP swaps inside rows of 16,
+// then row swaps): every lane ends with the same bits.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp_move<0xB1>(v));    // quad_perm 1,0,3,2
+  v = fmaxf(v, dpp_move<0x4E>(v));    // quad_perm 2,3,0,1
+  v = fmaxf(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
@@ -41,26 +59,34 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
                                                     int H, int Dh, uint16_t* __restrict__ out,
                                                     float* __restrict__ out_lse) {
   const int lane = threadIdx.x & 63;
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);   // (token, head)
-  if (item >= (long long)n_tok * H) return;
-  const int h = (int)(item % H);
-  const int t = (int)(item / H);
+  // (token, head); the host keeps n_tok * H * 64 below 2^32, so 32-bit division
+  const unsigned item = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (item >= (unsigned)n_tok * (unsigned)H) return;
+  const int h = (int)(item % (unsigned)H);
+  const int t = (int)(item / (unsigned)H);
+  const int q4 = Dh / 4;
+  const size_t sstride = (size_t)H * Dh;   // floats from one partition to the next
+  const float* obase = part_o + ((size_t)t * S * H + h) * Dh;
+  // slices of lanes past the head re-read its last slice and store nothing;
+  // partitions past S re-read the last one with weight 0
+  auto load8 = [&](f32x4 (&v)[8], int s0, int d4) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(obase + (size_t)min(s0 + u, S - 1) * sstride + 4 * d4);
+  };
+  f32x4 v[8];
+  load8(v, 0, min(lane, q4 - 1));
   const float l = lane < S ? part_lse[((size_t)t * S + lane) * H + h] : -INFINITY;
   const float M = wave_max(l);
   const bool any = M != -INFINITY;
   const float w = (any && l != -INFINITY) ? __builtin_amdgcn_exp2f((l - M) * kLog2e) : 0.f;
-  const float L = wave_sum(w);   // butterfly: every lane holds the same bits
+  const float L = wave_sum(w);
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const int q4 = Dh / 4;
-  for (int d4 = lane; d4 < q4; d4 += 64) {
+  for (int d4b = 0; d4b < q4; d4b += 64) {
+    const int d4 = min(d4b + lane, q4 - 1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += 8) {
-      f32x4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sc = min(s0 + u, S - 1);   // past S: re-read the last partition, weight 0
-        v[u] = *reinterpret_cast<const f32x4*>(part_o + (((size_t)t * S + sc) * H + h) * Dh + 4 * d4);
-      }
+      if (d4b > 0 || s0 > 0) load8(v, s0, d4);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(s0 + u, 63)));
@@ -68,10 +94,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
         acc += v[u] * wgt;
       }
     }
-    uint2 o;
-    o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<uint2*>(out + ((size_t)t * H + h) * Dh + 4 * d4) = o;
+    if (d4b + lane < q4) {
+      uint2 o;
+      o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<uint2*>(out + ((size_t)t * H + h) * Dh + 4 * d4) = o;
+    }
   }
   if (out_lse != nullptr && lane == 0)
     out_lse[(size_t)t * H + h] = L > 0.f ? M + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
