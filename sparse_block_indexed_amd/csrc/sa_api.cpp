@@ -120,15 +120,15 @@ size_t sa_indexer_topk_workspace_size(int n_tok, int max_pages_per_seq, int topk
 int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits) {
   if (num_splits > 0) return std::min(num_splits, SA_MAX_SPLITS);
   // Reach about one workgroup per CU while giving every wave of a workgroup at
-  // least two 4-block chunks: a chunk costs about one memory round trip when
-  // few workgroups run, so tiny grids want short partitions, but extra
-  // partitions cost partial-result traffic and a merge launch (one chunk per
-  // wave measured no faster than two, and a split grid that already fills the
-  // GPU measured slower than an unsplit one).
+  // least one 4-block chunk: a chunk costs about one memory round trip when
+  // few workgroups run, so tiny grids want short partitions (a one-token
+  // window call: 9.2 us at 2 partitions, 8.1 us at 4), while a split grid that
+  // already fills the GPU measured slower than an unsplit one (partial-result
+  // traffic and a merge launch).
   const int work = std::max(1, n_tok) * sa::kGroups;
   const int want = (256 + work - 1) / work;
   const int chunks = (std::max(1, max_blocks_per_token) + 3) / 4;
-  const int cap = std::max(1, chunks / 8);
+  const int cap = std::max(1, chunks / 4);
   return std::max(1, std::min(std::min(want, cap), SA_MAX_SPLITS));
 }
 

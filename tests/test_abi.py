@@ -61,11 +61,11 @@ def test_workspace_size(lib):
 def test_resolve_num_splits(lib):
     r = lib.sa_resolve_num_splits
     assert r(256, 513, 0) == 1          # 128K verify batch: the grid already fills the GPU
-    assert r(1, 513, 0) == 16           # one token: 129 chunks over 16 partitions (2 chunks per wave)
+    assert r(1, 513, 0) == 32           # one token: 129 chunks over 32 partitions (1 chunk per wave)
     assert r(64, 66, 0) == 1            # sliding window, batch 64: one workgroup per (token, group)
     assert r(4, 513, 0) == 16
     assert r(16, 513, 0) == 4           # the grid reaches 256 workgroups first
-    assert r(1, 66, 0) == 2             # one-token window: 17 chunks
+    assert r(1, 66, 0) == 4             # one-token window: 17 chunks
     assert r(1, 1, 0) == 1              # nothing to split
     assert r(3, 513, 7) == 7            # explicit value kept
     assert r(3, 513, 1000) == 64        # clamped

@@ -171,6 +171,31 @@ def test_invalid_tokens_attend_nothing():
     _check_all(wl, sel, out, lse, [3], what="valid neighbour")
 
 
+def test_invalid_positions_on_the_long_select_paths():
+    """Tokens whose position is at or past their sequence's length but inside
+    the page table, so that their rows are located and scored: one on the fused
+    select (history above topk), one on the long-history select (score-pass
+    histogram, collect, candidate list; history above 16K blocks). Both select
+    nothing and attend nothing, in the sparse and the window layer; every other
+    token matches the oracle."""
+    _say("invalid positions, long select paths")
+    from gpu_helpers import run_swa
+    spec = I.WorkloadSpec("inv_long", batch=2, seq_lens=[140000, 6000], q_per_seq=3)
+    wl = I.make_workload(spec, seed=25, device="cuda")
+    assert wl.max_pages_per_seq * 64 > 139000
+    t1 = [t for t in range(wl.n_tok) if int(wl.q_seq[t]) == 1]
+    bad = t1[:2]
+    wl.q_pos[bad[0]] = 9000        # 1,125 historical blocks: fused select
+    wl.q_pos[bad[1]] = 139000      # 17,375 historical blocks: long-history select
+    sel, out, lse = run_sparse_layer(wl)
+    wout, wlse = run_swa(wl)
+    for t in bad:
+        assert (sel[t] == -1).all(), f"token {t} selected blocks"
+        assert (out[t] == 0).all() and torch.isneginf(lse[t]).all()
+        assert (wout[t] == 0).all() and torch.isneginf(wlse[t]).all()
+    _check_all(wl, sel, out, lse, [t for t in range(wl.n_tok) if t not in bad], what="valid tokens")
+
+
 def test_poison_unread_blocks_and_future_positions():
     """NaN in every K/V block that is neither selected nor current, and in the
     current block past the query position: outputs bit-identical."""
