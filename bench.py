@@ -298,6 +298,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="BLAS threads for the oracle baseline (0: the process default)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after a 1 GiB write that evicts L2/MALL (reported separately)")
     ap.add_argument("--workload", type=int, default=1, choices=range(5),
@@ -501,11 +503,17 @@ def main():
     if cold_ms is not None:
         result["cold_cache"] = {"ms_per_step": cold_ms, "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, sel_host, window,
-                                              kv_fp8=(kc, vc, kv_kw["k_scale"], kv_kw["v_scale"])
-                                              if args.fp8_kv else None,
-                                              q_groups=qidx if per_group else None,
-                                              kidx_fp8=kidx if args.fp8_index_keys else None)
+        import contextlib
+        limit = contextlib.nullcontext()
+        if args.cpu_threads > 0:   # cap the oracle's BLAS threads (e.g. 1 for a one-core figure)
+            from threadpoolctl import threadpool_limits
+            limit = threadpool_limits(limits=args.cpu_threads)
+        with limit:
+            result["cpu_baseline"] = cpu_baseline(wl, sel_host, window,
+                                                  kv_fp8=(kc, vc, kv_kw["k_scale"], kv_kw["v_scale"])
+                                                  if args.fp8_kv else None,
+                                                  q_groups=qidx if per_group else None,
+                                                  kidx_fp8=kidx if args.fp8_index_keys else None)
     print(json.dumps(result), flush=True)
 
 
