@@ -177,8 +177,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   {
     constexpr int kFill = kFillSlots / kThreads;
     const int32_t* prow = a.page_table + (size_t)(in_range ? b : 0) * a.max_pages;
-    const int32_t* srow =
-        a.sel_idx + ((size_t)t * (a.sel_per_group ? kGroups : 1) + (a.sel_per_group ? g : 0)) * a.topk;
+    const int32_t* srow = kWindow ? nullptr   // (a window call has no block-id table)
+        : a.sel_idx + ((size_t)t * (a.sel_per_group ? kGroups : 1) + (a.sel_per_group ? g : 0)) * a.topk;
     int beta[kFill];
     bool ok[kFill];
 #pragma unroll
