@@ -8,10 +8,11 @@ last 4 positions of each as query tokens (256 tokens), bf16 paged KV with
 randomly permuted 64-token pages, integer index inputs in [-4, 4], Q/K/V ~ N(0,1).
 Inputs are resident in HBM before timing starts.
 
-`--workload N` runs one of the other workloads instead (0: decode at 8K,
-batch 1; 2: sliding-window decode at 16K-32K, batch 64; 3: decode at 1M,
-batch 4; 4: a 16,384-token prefill chunk after 112K tokens); the default is
-the headline workload 1.
+`--workload NAME` runs one of the other workloads instead (decode_8k_b1:
+decode at 8K, batch 1; swa_decode_32k_b64: sliding-window decode at
+16K-32K, batch 64; decode_1m_b4: decode at 1M, batch 4;
+prefill_chunk_16k_at_112k: a 16,384-token prefill chunk after 112K tokens);
+the default is the headline mtp_verify_128k_b64.
 
 The step is captured as HIP graphs and replayed, 10 steps per replay as a
 served forward replays its layers (`--eager` issues every call from Python
@@ -199,8 +200,12 @@ def time_phase(fn, steps: int, eager: bool, stream, reps: int = 5) -> float:
     return float(np.mean(times))
 
 
-NAMES = {0: "decode_8k_b1", 1: "mtp_verify_128k_b64", 2: "swa_decode_32k_b64", 3: "decode_1m_b4",
-         4: "prefill_chunk_16k_at_112k"}
+WORKLOAD_NAMES = ("decode_8k_b1", "mtp_verify_128k_b64", "swa_decode_32k_b64", "decode_1m_b4",
+                  "prefill_chunk_16k_at_112k")
+HEADLINE = "mtp_verify_128k_b64"
+WINDOW_WORKLOAD = "swa_decode_32k_b64"        # the sliding-window layer
+LONG_CONTEXT_WORKLOAD = "decode_1m_b4"        # the index-key scan dominates its bytes
+PREFILL_WORKLOAD = "prefill_chunk_16k_at_112k"  # reported against the MFMA peak
 
 
 def layer_group(args, wl, dev):
@@ -215,12 +220,12 @@ def layer_group(args, wl, dev):
     from sparse_block_indexed_amd import bytes_model as B
     from sparse_block_indexed_amd import inputs as I
     from sparse_block_indexed_amd import ops
-    W = args.workload
+    name = args.workload
     if args.fp8_kv or args.per_group_selection or args.fp8_index_keys:
         raise SystemExit("--layer-group runs the bf16 layers only")
     n_tok, topk, window = wl.n_tok, 512, 512
     pt, sl, qs, qp = wl.device_ints(dev)
-    layers = [I.layer_inputs(wl, seed=7000 + 10 * W + i) for i in range(3)] + [wl]
+    layers = [I.layer_inputs(wl, seed=7000 + 10 * I.WORKLOADS[name][1] + i) for i in range(3)] + [wl]
     Sw = ops.resolve_num_splits(n_tok, window // 8 + 2, args.num_splits)
     Ss = ops.resolve_num_splits(n_tok, topk + 1, args.num_splits)
     f32 = dict(dtype=torch.float32, device=dev)
@@ -272,12 +277,12 @@ def layer_group(args, wl, dev):
              "sparse_decode": "attention_kernel<false, bf16>%s (sa_sparse_decode)" % (" + merge_kernel" if Ss > 1 else "")}
     group_bytes = sum(count[k] * nbytes[k] for k in nbytes)
     return {
-        "metric": f"{NAMES[W]} hybrid layer group (3 window + 1 sparse layer) query-tokens/s; achieved HBM GB/s",
+        "metric": f"{name} hybrid layer group (3 window + 1 sparse layer) query-tokens/s; achieved HBM GB/s",
         "value": n_tok / (ms * 1e-3),
         "unit": "query-tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": NAMES[W] + "_layer_group", "layers": "3 x window 512 + 1 x sparse top-512",
+        "config": {"workload": name + "_layer_group", "layers": "3 x window 512 + 1 x sparse top-512",
                    "batch": wl.batch, "query_tokens": n_tok, "num_splits_window": Sw, "num_splits_sparse": Ss,
                    "kv_cache": "bf16", "launch": "eager" if args.eager else "hip_graph"},
         "eager_ms_per_step": ms_eager,
@@ -302,9 +307,8 @@ def main():
                     help="BLAS threads for the oracle baseline (0: the process default)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after a 1 GiB write that evicts L2/MALL (reported separately)")
-    ap.add_argument("--workload", type=int, default=1, choices=range(5),
-                    help="0 decode 8K b1, 1 MTP verify 128K b64 (default), 2 SWA 32K b64, 3 decode 1M b4, "
-                         "4 prefill chunk 16K after 112K")
+    ap.add_argument("--workload", default=HEADLINE, choices=WORKLOAD_NAMES,
+                    help="the workload (default: the headline %s)" % HEADLINE)
     ap.add_argument("--num-splits", type=int, default=0,
                     help="partitions per (token, group) for the attention call; 0 lets the library pick")
     ap.add_argument("--fp8-index-keys", action="store_true",
@@ -323,8 +327,8 @@ def main():
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (see the sharding notes in "
-              "DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -346,15 +350,16 @@ def main():
     from sparse_block_indexed_amd import ops
 
     ops.load_library()
-    W = args.workload
-    wl = I.config_workload(W, device=dev)
+    assert set(WORKLOAD_NAMES) == set(I.WORKLOADS)
+    name = args.workload
+    wl = I.named_workload(name, device=dev)
     if args.layer_group:
         print(json.dumps(layer_group(args, wl, dev)), flush=True)
         return
     pt, sl, qs, qp = wl.device_ints(dev)
     kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if args.fp8_index_keys else wl.k_idx_cache
     per_group = args.per_group_selection
-    qidx = I.grouped_index_queries(wl.n_tok, seed=1000 + W, device=dev) if per_group else wl.q_idx
+    qidx = I.grouped_index_queries(wl.n_tok, seed=1000 + I.WORKLOADS[name][1], device=dev) if per_group else wl.q_idx
     if args.fp8_kv:
         k_scale, v_scale = 1.0 / 32, 1.0 / 16
         kc, vc = I.quantize_kv_fp8(wl.k_cache, wl.v_cache, k_scale, v_scale)
@@ -362,7 +367,7 @@ def main():
     else:
         kc, vc, kv_kw = wl.k_cache, wl.v_cache, {}
     topk = 512
-    window = 512 if W == 2 else None
+    window = 512 if name == WINDOW_WORKLOAD else None
     n_tok = wl.n_tok
     max_blocks = (window // 8 + 2) if window else topk + 1
     S = ops.resolve_num_splits(n_tok, max_blocks, args.num_splits)
@@ -440,8 +445,7 @@ def main():
         attn_bytes = B.swa_attention_bytes(wl.q_seq, wl.q_pos, window, kv_bytes=kvb)
         idx_bytes, idx_flops = 0, 0
         attn_flops = B.swa_attention_flops(wl.q_pos, window)
-    names = NAMES
-    config = {"workload": names[W], "batch": wl.batch, "query_tokens": n_tok,
+    config = {"workload": name, "batch": wl.batch, "query_tokens": n_tok,
               "context": (f"uniform [{wl.spec.seq_len_range[0]}, {wl.spec.seq_len_range[1]}]"
                           if wl.spec.seq_len_range else str(sorted(set(int(x) for x in wl.seq_lens)))),
               "block_tokens": 8, "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S}
@@ -455,8 +459,8 @@ def main():
         config["window"] = window
     tags = [t for t, on in (("fp8 index keys", args.fp8_index_keys), ("fp8 KV", args.fp8_kv),
                             ("per-KV-group selection", per_group)) if on]
-    metric = METRIC if (W == 1 and not tags) else \
-        f"{names[W]}{' (' + ', '.join(tags) + ')' if tags else ''} query-tokens/s; achieved HBM GB/s"
+    metric = METRIC if (name == HEADLINE and not tags) else \
+        f"{name}{' (' + ', '.join(tags) + ')' if tags else ''} query-tokens/s; achieved HBM GB/s"
     result = {
         "metric": metric,
         "value": n_tok / (ms_per_step * 1e-3),
@@ -481,14 +485,14 @@ def main():
                                                    " + merge_kernel" if S > 1 else "",
                                                    "sa_swa_decode" if window else "sa_sparse_decode",
                                                    "_fp8kv" if args.fp8_kv else "")
-    if W == 4:
+    if name == PREFILL_WORKLOAD:
         # the prefill chunk is a dense-contraction workload on paper: report MFMA utilisation
         tf = (attn_flops + idx_flops) / (ms_per_step * 1e-3) / 1e12
         result["mfma_utilisation"] = tf / (PEAK_BF16_TFLOPS)
         attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": kname}
-    elif W == 3:
+    elif name == LONG_CONTEXT_WORKLOAD:
         # at 1M context the index-key scan is the dominant read
         achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -498,7 +502,7 @@ def main():
         achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                               "frac": achieved / PEAK_HBM_GBPS,
-                              "traffic": counter_traffic() if (W == 1 and not args.fp8_kv) else None,
+                              "traffic": counter_traffic() if (name == HEADLINE and not tags) else None,
                               "kernel": kname}
     if cold_ms is not None:
         result["cold_cache"] = {"ms_per_step": cold_ms, "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}

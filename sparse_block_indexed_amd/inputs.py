@@ -68,15 +68,19 @@ class WorkloadSpec:
     spare_pages: int = 0
 
 
-# The five workloads: decode at 8K, MTP verify at 96K-128K (the headline),
-# sliding-window decode at 16K-32K, decode at 1M, and a 16K prefill chunk.
-CONFIGS = [
-    WorkloadSpec("decode_8k_b1", batch=1, seq_lens=[8192], q_per_seq=1, identity_pages=True),
-    WorkloadSpec("mtp_verify_128k_b64", batch=64, seq_len_range=(98304, 131072), q_per_seq=4),
-    WorkloadSpec("swa_decode_32k_b64", batch=64, seq_len_range=(16384, 32768), q_per_seq=1),
-    WorkloadSpec("decode_1m_b4", batch=4, seq_lens=[1048576] * 4, q_per_seq=1),
-    WorkloadSpec("prefill_chunk_16k_at_112k", batch=1, seq_lens=[131072], q_per_seq=16384),
-]
+# The five workloads, by name, with their default seeds: decode at 8K, MTP
+# verify at 96K-128K (the headline), sliding-window decode at 16K-32K, decode
+# at 1M, and a 16K prefill chunk.
+WORKLOADS = {
+    "decode_8k_b1": (WorkloadSpec("decode_8k_b1", batch=1, seq_lens=[8192], q_per_seq=1, identity_pages=True), 0),
+    "mtp_verify_128k_b64": (WorkloadSpec("mtp_verify_128k_b64", batch=64, seq_len_range=(98304, 131072),
+                                         q_per_seq=4), 1),
+    "swa_decode_32k_b64": (WorkloadSpec("swa_decode_32k_b64", batch=64, seq_len_range=(16384, 32768),
+                                        q_per_seq=1), 2),
+    "decode_1m_b4": (WorkloadSpec("decode_1m_b4", batch=4, seq_lens=[1048576] * 4, q_per_seq=1), 3),
+    "prefill_chunk_16k_at_112k": (WorkloadSpec("prefill_chunk_16k_at_112k", batch=1, seq_lens=[131072],
+                                               q_per_seq=16384), 4),
+}
 
 
 @dataclasses.dataclass
@@ -198,9 +202,10 @@ def grouped_index_queries(n_tok: int, seed: int, device="cpu", lo: int = -4, hi:
     return _randint_bf16((n_tok, G, DI), lo, hi, gen, torch.device(device))
 
 
-def config_workload(index: int, device="cpu", seed: Optional[int] = None) -> Workload:
-    """One of the five named workloads; the seed defaults to the workload's index."""
-    return make_workload(CONFIGS[index], index if seed is None else seed, device)
+def named_workload(name: str, device="cpu", seed: Optional[int] = None) -> Workload:
+    """One of the five named workloads (WORKLOADS), with its default seed unless one is given."""
+    spec, default_seed = WORKLOADS[name]
+    return make_workload(spec, default_seed if seed is None else seed, device)
 
 
 # ---------------------------------------------------------------------------

@@ -90,11 +90,11 @@ def test_fp8kv_small_mixed_swa(window, num_splits):
                          np.stack([r[1] for r in refs]), f"fp8kv swa W={window}")
 
 
-def test_fp8kv_config1_mtp_verify_128k():
+def test_fp8kv_mtp_verify_128k_b64():
     """The headline workload at full size, default launch configuration;
     attention on a sample of 16 tokens."""
-    _say("fp8kv config 1")
-    wl = I.config_workload(1, device="cuda")
+    _say("fp8kv mtp_verify_128k_b64")
+    wl = I.named_workload("mtp_verify_128k_b64", device="cuda")
     kv = _quantize(wl)
     sel, out, lse = run_sparse_layer(wl, kv_fp8=kv)
     rng = np.random.default_rng(0)
@@ -102,9 +102,9 @@ def test_fp8kv_config1_mtp_verify_128k():
     _check_sparse(wl, kv, sel, out, lse, sample, what="fp8kv mtp_verify_128k")
 
 
-def test_fp8kv_config2_swa_32k():
-    _say("fp8kv config 2")
-    wl = I.config_workload(2, device="cuda")
+def test_fp8kv_swa_decode_32k_b64():
+    _say("fp8kv swa_decode_32k_b64")
+    wl = I.named_workload("swa_decode_32k_b64", device="cuda")
     kv = _quantize(wl)
     out, lse = run_swa(wl, kv_fp8=kv)
     ov = OracleView(wl, kv_fp8=kv)

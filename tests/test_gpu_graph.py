@@ -128,10 +128,10 @@ def test_long_history_step_graph_replays_match_eager():
     _graph_vs_eager(wl, 0)
 
 
-def test_config1_step_graph_replays_match_eager():
+def test_mtp_verify_step_graph_replays_match_eager():
     """The 128K MTP verify workload as the benchmark replays it."""
-    _say("graph config 1")
-    wl = I.config_workload(1, device="cuda")
+    _say("graph mtp_verify_128k_b64")
+    wl = I.named_workload("mtp_verify_128k_b64", device="cuda")
     _graph_vs_eager(wl, 0, replays=2)
 
 

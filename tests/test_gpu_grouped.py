@@ -91,11 +91,11 @@ def test_grouped_with_equal_queries_equals_shared_path():
         assert torch.equal(og, os_) and torch.equal(lg, ls)
 
 
-def test_grouped_config1_mtp_verify_128k():
+def test_grouped_mtp_verify_128k_b64():
     """The 128K verify workload with per-group queries: selections of 64 tokens
     (all 4 groups), attention of 16."""
-    _say("grouped config 1")
-    wl = I.config_workload(1, device="cuda")
+    _say("grouped mtp_verify_128k_b64")
+    wl = I.named_workload("mtp_verify_128k_b64", device="cuda")
     qg = I.grouped_index_queries(wl.n_tok, seed=9, device="cuda")
     sel, out, lse = _run(wl, qg)
     rng = np.random.default_rng(1)
@@ -128,11 +128,11 @@ def test_grouped_prefill_gemm_and_long_histories():
         _check(wl, qg, sel, out, lse, toks, toks[:6], what=spec.name)
 
 
-def test_grouped_config1_fp8_keys_takes_the_16_row_scorer():
+def test_grouped_mtp_verify_fp8_keys_takes_the_16_row_scorer():
     """Per-group queries of the 128K workload (16 rows per sequence) with
     one-byte keys: the 16-row MFMA scorer; selections of 32 tokens."""
-    _say("grouped config 1 fp8 keys")
-    wl = I.config_workload(1, device="cuda")
+    _say("grouped mtp_verify_128k_b64, fp8 keys")
+    wl = I.named_workload("mtp_verify_128k_b64", device="cuda")
     qg = I.grouped_index_queries(wl.n_tok, seed=10, device="cuda")
     codes = I.fp8_e4m3_codes(wl.k_idx_cache)
     sel, out, lse = _run(wl, qg, kidx=codes)

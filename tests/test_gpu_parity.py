@@ -80,18 +80,18 @@ def test_small_topk_values(topk):
     _check_all(wl, sel, out, lse, range(wl.n_tok), topk=topk, what=f"topk={topk}")
 
 
-def test_config0_decode_8k():
-    _say("config 0")
-    wl = I.config_workload(0, device="cuda")
+def test_decode_8k_b1():
+    _say("decode_8k_b1")
+    wl = I.named_workload("decode_8k_b1", device="cuda")
     sel, out, lse = run_sparse_layer(wl)
     _check_all(wl, sel, out, lse, range(wl.n_tok), what="decode_8k")
 
 
-def test_config1_mtp_verify_128k():
+def test_mtp_verify_128k_b64():
     """The headline workload at full size in the bench's launch configuration:
     every token's selection is checked; attention on a sample of 16 tokens."""
-    _say("config 1")
-    wl = I.config_workload(1, device="cuda")
+    _say("mtp_verify_128k_b64")
+    wl = I.named_workload("mtp_verify_128k_b64", device="cuda")
     sel, out, lse = run_sparse_layer(wl)
     ov = OracleView(wl)
     sel_h = sel.cpu().numpy()
@@ -102,9 +102,9 @@ def test_config1_mtp_verify_128k():
     _check_all(wl, sel, out, lse, sample, what="mtp_verify_128k")
 
 
-def test_config2_swa_32k():
-    _say("config 2")
-    wl = I.config_workload(2, device="cuda")
+def test_swa_decode_32k_b64():
+    _say("swa_decode_32k_b64")
+    wl = I.named_workload("swa_decode_32k_b64", device="cuda")
     out, lse = run_swa(wl)
     ov = OracleView(wl)
     refs = [ov.swa(t) for t in range(wl.n_tok)]
@@ -112,16 +112,16 @@ def test_config2_swa_32k():
                          np.stack([r[1] for r in refs]), "swa_32k")
 
 
-def test_config3_decode_1m():
-    _say("config 3")
-    wl = I.config_workload(3, device="cuda")
+def test_decode_1m_b4():
+    _say("decode_1m_b4")
+    wl = I.named_workload("decode_1m_b4", device="cuda")
     sel, out, lse = run_sparse_layer(wl)
     _check_all(wl, sel, out, lse, range(wl.n_tok), what="decode_1m")
 
 
-def test_config4_prefill_chunk_sampled():
-    _say("config 4")
-    wl = I.config_workload(4, device="cuda")
+def test_prefill_chunk_16k_at_112k_sampled():
+    _say("prefill_chunk_16k_at_112k")
+    wl = I.named_workload("prefill_chunk_16k_at_112k", device="cuda")
     sel, out, lse = run_sparse_layer(wl)
     rng = np.random.default_rng(4)
     sample = sorted(set(rng.choice(wl.n_tok, size=12, replace=False).tolist()) | {0, wl.n_tok - 1})
@@ -232,7 +232,7 @@ def test_poison_unread_blocks_and_future_positions():
 
 def test_deterministic_and_batch_invariant():
     _say("determinism")
-    wl = I.config_workload(0, device="cuda", seed=31)
+    wl = I.named_workload("decode_8k_b1", device="cuda", seed=31)
     wl_big = I.make_workload(I.WorkloadSpec("bi", batch=5, seq_lens=[8192, 3000, 20000, 8192, 500], q_per_seq=1),
                              seed=32, device="cuda")
     # place config-0's sequence as sequence 3 of the bigger batch
@@ -252,7 +252,7 @@ def test_deterministic_and_batch_invariant():
 
 def test_split_count_changes_only_rounding():
     _say("splits")
-    wl = I.config_workload(0, device="cuda", seed=33)
+    wl = I.named_workload("decode_8k_b1", device="cuda", seed=33)
     ref = None
     for S in (1, 2, 5, 32, 64):
         sel, out, lse = run_sparse_layer(wl, num_splits=S)
@@ -373,13 +373,13 @@ def _check_selection(wl, sel, tokens, topk=512, kidx_fp8=None, what=""):
         assert sel_h[t].tolist() == ov.selection(t, topk).tolist(), f"{what}: token {t}"
 
 
-@pytest.mark.parametrize("cfg", [1, 3])
-def test_fp8_index_keys_match_bf16_and_oracle(cfg):
+@pytest.mark.parametrize("name", ["mtp_verify_128k_b64", "decode_1m_b4"])
+def test_fp8_index_keys_match_bf16_and_oracle(name):
     """Integer keys are exact in E4M3: the one-byte path must select exactly what
     the bf16 path and the oracle (decoding the codes itself) select."""
-    _say(f"fp8 keys config {cfg}")
+    _say(f"fp8 keys {name}")
     from sparse_block_indexed_amd import ops
-    wl = I.config_workload(cfg, device="cuda")
+    wl = I.named_workload(name, device="cuda")
     pt, sl, qs, qp = device_tables(wl)
     codes = I.fp8_e4m3_codes(wl.k_idx_cache)
     sel8 = ops.indexer_topk(wl.q_idx, codes, pt, sl, qs, qp, 512)
@@ -387,7 +387,7 @@ def test_fp8_index_keys_match_bf16_and_oracle(cfg):
     torch.cuda.synchronize()
     assert torch.equal(sel8, sel16)
     sample = range(wl.n_tok) if wl.n_tok <= 8 else range(0, wl.n_tok, 16)
-    _check_selection(wl, sel8, sample, kidx_fp8=codes, what=f"fp8 cfg{cfg}")
+    _check_selection(wl, sel8, sample, kidx_fp8=codes, what=f"fp8 keys {name}")
 
 
 def test_fp8_index_keys_general_codes():
