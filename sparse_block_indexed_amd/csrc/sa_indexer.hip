@@ -28,9 +28,10 @@
 //               register-held scores for short histories), everything above the
 //               threshold bin is chosen; within the threshold bin the needed
 //               keys are taken by rank (larger key, then lower block id) or, for
-//               large bins, by two more radix levels and a tie walk in block
-//               order; the chosen ids are written ascending from a bitmap. A row
-//               whose threshold bin or candidate list overflows takes an ordered
+//               large bins, by two more radix levels, the ids tied at the exact
+//               threshold being taken in block order; one scan over the bitmaps
+//               places every chosen id, written ascending. A row whose
+//               threshold bin or candidate list overflows takes an ordered
 //               select over all of its scores instead.
 
 #include <algorithm>

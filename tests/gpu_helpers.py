@@ -138,8 +138,8 @@ def bf16_to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def assert_close_outputs(got_out, got_lse, ref_out, ref_lse, what=""):
-    """North-star tolerance: max-abs 2e-2 and relative RMS 5e-3 over the compared set;
-    lse within 1e-3."""
+    """The output tolerance: max-abs 2e-2 and relative RMS 5e-3 over the compared
+    set against the fp64 oracle; lse within 1e-3."""
     got_out = np.asarray(got_out, dtype=np.float64)
     ref_out = np.asarray(ref_out, dtype=np.float64)
     assert np.isfinite(got_out).all(), f"{what}: non-finite output"
