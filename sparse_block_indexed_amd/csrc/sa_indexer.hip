@@ -945,13 +945,6 @@ __device__ void select_ordered_global(const IndexerArgs& a, FinalizeLds& s, int 
   }
 }
 
-// Per token. The histogram bin b1 that holds the k-th largest score splits the
-// scores into "surely chosen" (bin above b1; fewer than k) and the threshold
-// bin. Two more radix levels over the threshold bin's keys give the exact k-th
-// key tau; keys above tau are chosen, and keys equal to tau are chosen in block
-// order until k are taken (a bitmap walk). The chosen ids are written ascending
-// by walking the selection bitmap. Short histories read their scores directly,
-// long ones the candidates gathered by collect_kernel.
 // Histogram and classification of one token's scores. KP > 0: a history of
 // at most KP * kFinalThreads blocks whose scores are held in registers, KP per
 // thread (instantiated for 2 .. 32 so that short histories execute no steps
@@ -1082,6 +1075,13 @@ __device__ __forceinline__ ClassifyResult finalize_classify(const IndexerArgs& a
   return kClassified;
 }
 
+// Per token. The histogram bin b1 that holds the k-th largest score splits the
+// scores into "surely chosen" (bins above b1; fewer than k) and the threshold
+// bin. Ranking the threshold bin's entries, or two more radix levels over their
+// keys, completes the selection: keys above the exact k-th key tau are chosen,
+// and keys equal to tau in block order until k are taken. emit_selection writes
+// the chosen ids ascending. Short histories read their scores directly, long
+// ones the candidates gathered by collect_kernel.
 __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) {
   __shared__ FinalizeLds s;
   extern __shared__ uint32_t s_bm[];   // [2][bitmap_words]: chosen ids, ids tied at tau
