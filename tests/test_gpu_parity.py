@@ -444,6 +444,20 @@ def test_sixteen_row_mfma_scorer_mixed_sequences(fp8_keys):
         assert torch.equal(part, sel[t0:t1])
 
 
+def test_finalize_step_count_boundaries():
+    """The fused select runs the instantiation sized to the row's history: 2, 4,
+    8, 16 or 32 scores per thread of 512, so rows of 1,024 / 2,048 / 4,096 /
+    8,192 blocks are the largest the first four hold. One row on either side of
+    every boundary, all in one call, checked against the oracle."""
+    _say("finalize step boundaries")
+    hist = [1024, 1025, 2048, 2049, 4096, 4097, 8192, 8193]
+    wl = I.make_workload(I.WorkloadSpec("steps", batch=len(hist), seq_lens=[8 * h + 1 for h in hist], q_per_seq=1),
+                         seed=52, device="cuda")
+    assert sorted(int(p) // 8 for p in wl.q_pos) == hist
+    sel, out, lse = run_sparse_layer(wl)
+    _check_all(wl, sel, out, lse, range(wl.n_tok), what="finalize step boundaries")
+
+
 def test_history_limits_of_the_select_paths():
     """Around the select paths' size limits, every selection checked against
     the oracle: a call whose longest history is exactly 16,384 blocks (scores
