@@ -449,12 +449,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
 // their sequence's history. Wave w computes tokens 16w..16w+15 against each
 // 32-block key tile with v_mfma_f32_16x16x32_bf16 (A = index queries, held in
 // registers; B = keys, staged through LDS rows padded to 528 bytes so that the
-// 16-byte fragment reads of 16 lanes hit 64 distinct banks). The next tile's
-// keys are loaded into registers while the current tile is multiplied. Rows of
+// 16-byte fragment reads of 16 lanes hit 64 distinct banks). The page ids of
+// the workgroup's block range are read into LDS once per pass, so a tile's key
+// loads depend on no other global read; they are issued two tiles ahead (two
+// register sets), and one barrier per tile orders the LDS buffers. Rows of
 // another sequence than the one being processed are handled in further passes.
 constexpr int kGemmTokens = 64;
 constexpr int kGemmBlocks = 32;
 constexpr int kKeyStride = kKeyBytes + 16;
+constexpr int kGemmMaxTiles = kFuseLimit / kGemmBlocks;           // tiles of the longest history
+constexpr int kGemmPages = kGemmMaxTiles * kGemmBlocks / kBlocksPerPage;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -468,6 +472,7 @@ template <bool kFp8>
 __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int tiles_per_wg) {
   constexpr int KB = KeyFmt<kFp8>::kBytes;
   __shared__ uint8_t s_keys[2][kGemmBlocks * kKeyStride];
+  __shared__ int s_pages[kGemmPages];   // pass's pages, from its first tile on; -1 = unreadable
   __shared__ int s_tok_cb[kGemmTokens];
   __shared__ int s_tok_seq[kGemmTokens];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 15, lg = lane >> 4;
@@ -505,28 +510,37 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
     for (int r = 0; r < kGemmTokens; ++r)
       if (((done >> r) & 1ull) == 0 && s_tok_seq[r] == seq) active |= 1ull << r;
     done |= active;
-    const int32_t* prow = a.page_table + (size_t)seq * a.max_pages;
     const int ntiles = (hi + kGemmBlocks - 1) / kGemmBlocks;
     const int tl0 = tile0, tl1 = min(ntiles, tile0 + tiles_per_wg);
     if (tl0 >= tl1) continue;
+    // page ids of blocks tl0*32 .. min(hi, tl1*32) - 1 (every page index < max_pages: hi <= p/8)
+    const int pg0 = tl0 * (kGemmBlocks / kBlocksPerPage);
+    const int npg = min((tl1 - tl0) * (kGemmBlocks / kBlocksPerPage), (hi + kBlocksPerPage - 1) / kBlocksPerPage - pg0);
+    {
+      const int32_t* prow = a.page_table + (size_t)seq * a.max_pages + pg0;
+      for (int i = tid; i < npg; i += kThreads) {
+        const int pg = prow[i];
+        s_pages[i] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
+      }
+    }
+    __syncthreads();
     // key tile staging: thread tid moves 16-byte pieces tid + 256*j of the
     // tile's keys (bf16: 8 dims per piece; fp8: 16 dims, widened to bf16 in LDS)
     constexpr int kPieces = kGemmBlocks * (KB / 16) / kThreads;
     constexpr int kPerKey = KB / 16;
-    u32x4 kreg[kPieces];
-    auto fetch = [&](int tile) {
+    u32x4 ra[kPieces], rb[kPieces];
+    auto fetch = [&](int tile, u32x4 (&kreg)[kPieces]) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
         const int piece = tid + kThreads * j;
         const int blk = piece / kPerKey, part = piece % kPerKey;
         const int beta = tile * kGemmBlocks + blk;
-        int page = beta < hi ? prow[beta >> 3] : -1;
-        const bool ok = page >= 0 && page < a.num_pages;
-        const size_t off = ok ? ((size_t)page * kBlocksPerPage + (beta & 7)) * KB + part * 16 : 0;
+        const int page = beta < hi ? s_pages[(beta >> 3) - pg0] : -1;
+        const size_t off = page >= 0 ? ((size_t)page * kBlocksPerPage + (beta & 7)) * KB + part * 16 : 0;
         kreg[j] = load16_stream(a.k_idx_cache + off);
       }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, const u32x4 (&kreg)[kPieces]) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
         const int piece = tid + kThreads * j;
@@ -547,12 +561,11 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
         }
       }
     };
-    fetch(tl0);
-    stash(0);
-    __syncthreads();
-    for (int tile = tl0; tile < tl1; ++tile) {
-      const int buf = (tile - tl0) & 1;
-      if (tile + 1 < tl1) fetch(tile + 1);
+    // One tile: its keys are in s_keys[buf]; `spare` held them (free now) and
+    // takes tile + 2; `next` holds tile + 1, stashed into the other buffer at
+    // the end. That buffer was last read before the previous tile's barrier.
+    auto step = [&](int tile, int buf, u32x4 (&spare)[kPieces], const u32x4 (&next)[kPieces]) {
+      if (tile + 2 < tl1) fetch(tile + 2, spare);
       constexpr int kSub = kGemmBlocks / 16;
       f32x4 c[kSub];
 #pragma unroll
@@ -567,28 +580,27 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
       }
       // c[n][r]: token row 16*wave + 4*lg + r, block tile*kGemmBlocks + 16*n + lq
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wave * 16 + 4 * lg + r;
-        if (((active >> row) & 1ull) == 0) continue;
-        const int t = t0 + row;
-        const int cbt = s_tok_cb[row];
-        float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+      for (int n = 0; n < kSub; ++n) {
+        const int beta = tile * kGemmBlocks + 16 * n + lq;
+        const bool readable = beta < hi && s_pages[(min(beta, hi - 1) >> 3) - pg0] >= 0;
 #pragma unroll
-        for (int n = 0; n < kSub; ++n) {
-          const int beta = tile * kGemmBlocks + 16 * n + lq;
-          if (beta < cbt) {
-            const int page = prow[beta >> 3];
-            srow[beta] = (page >= 0 && page < a.num_pages) ? c[n][r] : -INFINITY;
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int row = wave * 16 + 4 * lg + r;
+          if (((active >> row) & 1ull) && beta < s_tok_cb[row])
+            a.scores[(size_t)(t0 + row) * a.max_hist_blocks + beta] = readable ? c[n][r] : -INFINITY;
         }
       }
-      if (tile + 1 < tl1) {
-        __syncthreads();   // everyone is done reading the other buffer
-        stash(buf ^ 1);
-        __syncthreads();
-      }
-    }
+      if (tile + 1 < tl1) stash(buf ^ 1, next);
+      __syncthreads();
+    };
+    fetch(tl0, ra);
+    if (tl0 + 1 < tl1) fetch(tl0 + 1, rb);
+    stash(0, ra);
     __syncthreads();
+    for (int tile = tl0; tile < tl1; tile += 2) {
+      step(tile, 0, ra, rb);
+      if (tile + 1 < tl1) step(tile + 1, 1, rb, ra);
+    }
   }
 }
 
@@ -1197,10 +1209,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
   if (a.use_gemm) {
     const int ntt = (a.n_tok + kGemmTokens - 1) / kGemmTokens;
     const int ntiles = (a.max_hist_blocks + kGemmBlocks - 1) / kGemmBlocks;
-    // about two workgroups per CU: split the block tiles when there are few token tiles
+    // about three workgroups per CU (as many as fit in LDS): split the block
+    // tiles when there are few token tiles
     int splits = 1;
-    while (splits < ntiles && (long long)ntt * splits < 512) splits <<= 1;
-    const int per = (ntiles + splits - 1) / splits;
+    while (splits < ntiles && (long long)ntt * splits < 768) ++splits;
+    const int per = (ntiles + splits - 1) / splits;   // <= kGemmMaxTiles: the pass's page ids fit in LDS
     if (a.key_fp8)
       score_gemm_kernel<true><<<dim3((unsigned)ntt, (unsigned)splits), dim3(kThreads), 0, stream>>>(a, per);
     else

@@ -230,6 +230,52 @@ def test_poison_unread_blocks_and_future_positions():
     assert torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("q_per_seq,fp8_keys", [(2, False), (20, False), (70, False), (70, True)])
+def test_unreadable_pages_rank_last_and_are_skipped(q_per_seq, fp8_keys):
+    """Page-table entries outside [0, num_pages) (-1, and past the cache) on some
+    historical pages: their blocks score -inf, so they rank last (lower block
+    index first among them) and are chosen only when fewer readable blocks
+    exist; the attention skips their tokens. Covers the per-token scorer (2
+    tokens per sequence), the 16-row MFMA scorer (20) and the score GEMM (70)."""
+    _say(f"unreadable pages q_per_seq={q_per_seq} fp8={fp8_keys}")
+    from sparse_block_indexed_amd import ops
+    wl = I.make_workload(I.WorkloadSpec("bad_pages", batch=2, seq_lens=[3000, 9000], q_per_seq=q_per_seq),
+                         seed=61, device="cuda")
+    kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if fp8_keys else wl.k_idx_cache
+    ov = OracleView(wl, kidx_fp8=kidx if fp8_keys else None)   # reads keys through the intact table
+    bad = {0: [3, 10], 1: [0, 40, 100]}                         # logical pages, none holds a current block
+    pt_bad = wl.page_table.copy()
+    for b, pages in bad.items():
+        for i, lp in enumerate(pages):
+            pt_bad[b, lp] = -1 if i % 2 == 0 else wl.num_pages + 7
+    _, sl, qs, qp = device_tables(wl)
+    pt = torch.as_tensor(pt_bad, dtype=torch.int32, device="cuda")
+    sel = ops.indexer_topk(wl.q_idx, kidx, pt, sl, qs, qp, 512)
+    out, lse = ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE)
+    torch.cuda.synchronize()
+    sel_h = sel.cpu().numpy()
+    outs, refs, lses, rlses = [], [], [], []
+    for t in range(wl.n_tok):
+        b, p = int(wl.q_seq[t]), int(wl.q_pos[t])
+        cb = p // 8
+        assert all(lp != p // 64 for lp in bad[b])
+        q = O.bf16_to_f64(I.bf16_bits(wl.q_idx[t]))
+        scores = O.indexer_scores(q, ov.keys(b, cb))
+        for lp in bad[b]:
+            scores[8 * lp:min(8 * lp + 8, cb)] = -np.inf
+        ref_sel = O.select_top_blocks(scores, 512)
+        assert sel_h[t].tolist() == ref_sel.tolist(), f"token {t} selection differs"
+        if t % 9 == 0:
+            pos = O.sparse_token_positions(ref_sel, p)
+            pos = pos[~np.isin(pos // 64, bad[b])]
+            ro, rl = ov.attention(t, pos)
+            outs.append(bf16_to_np(out[t]))
+            lses.append(lse[t].cpu().numpy())
+            refs.append(ro)
+            rlses.append(rl)
+    assert_close_outputs(np.stack(outs), np.stack(lses), np.stack(refs), np.stack(rlses), "unreadable pages")
+
+
 def test_deterministic_and_batch_invariant():
     _say("determinism")
     wl = I.named_workload("decode_8k_b1", device="cuda", seed=31)
