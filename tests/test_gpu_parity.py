@@ -408,6 +408,22 @@ def test_prefill_gemm_path_mixed_tiles():
     _check_all(wl, sel, out, lse, [t for t in range(wl.n_tok) if t != 100], what="gemm mixed")
 
 
+def test_prefill_gemm_path_several_tiles_per_workgroup_and_passes():
+    """The score GEMM with 16K-block histories and 5 token tiles: each workgroup
+    scores 4 block tiles (both register sets of its pipeline, twice), and the
+    third token tile holds rows of both sequences (a second pass, which some
+    workgroups' tile ranges skip: the shorter history ends first)."""
+    _say("gemm several tiles per workgroup")
+    spec = I.WorkloadSpec("gemm_multi", batch=2, seq_lens=[131072, 70000], q_per_seq=160)
+    wl = I.make_workload(spec, seed=43, device="cuda")
+    sel, out, lse = run_sparse_layer(wl)
+    ov = OracleView(wl)
+    sel_h = sel.cpu().numpy()
+    for t in range(wl.n_tok):
+        assert sel_h[t].tolist() == ov.selection(t).tolist(), f"token {t} selection differs"
+    _check_all(wl, sel, out, lse, [0, 127, 159, 160, 200, 319], what="gemm several tiles")
+
+
 # ---------------------------------------------------------------------------
 # One-byte (OCP FP8 E4M3) index keys
 # ---------------------------------------------------------------------------
