@@ -113,6 +113,29 @@ def test_fp8kv_swa_decode_32k_b64():
                          np.stack([r[1] for r in refs]), "fp8kv swa_32k")
 
 
+def test_cacheable_loads_window_and_one_byte_kv():
+    """Calls with more than 64 query tokens per sequence (a prefill-like call)
+    read K/V with ordinary, cacheable loads instead of non-temporal ones: the
+    one-byte sparse layer and the window layer in both cache forms on that
+    path, against the oracle on sampled tokens (the window with 2 partitions
+    too)."""
+    _say("cacheable loads: fp8 sparse, window bf16 and fp8")
+    wl = I.make_workload(I.WorkloadSpec("cacheable", batch=2, seq_lens=[5000, 9000], q_per_seq=70),
+                         seed=95, device="cuda")
+    assert wl.n_tok > 64 * wl.batch
+    kv = _quantize(wl)
+    toks = list(range(0, wl.n_tok, 13)) + [wl.n_tok - 1]
+    sel, out, lse = run_sparse_layer(wl, kv_fp8=kv)
+    _check_sparse(wl, kv, sel, out, lse, toks, what="cacheable fp8kv sparse")
+    for form, kvf in (("bf16", None), ("fp8", kv)):
+        ov = OracleView(wl, kv_fp8=kvf)
+        refs = [ov.swa(t) for t in toks]
+        for S in (0, 2):
+            out, lse = run_swa(wl, num_splits=S, kv_fp8=kvf)
+            assert_close_outputs(bf16_to_np(out[toks]), lse[toks].cpu().numpy(), np.stack([r[0] for r in refs]),
+                                 np.stack([r[1] for r in refs]), f"cacheable swa {form} S={S}")
+
+
 def test_fp8kv_general_codes():
     """Every finite E4M3 code (subnormals, both signs, up to +-448) in K and V:
     checks the hardware's decoding of each code against the oracle's."""
