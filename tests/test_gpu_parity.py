@@ -520,6 +520,24 @@ def test_finalize_step_count_boundaries():
     _check_all(wl, sel, out, lse, range(wl.n_tok), what="finalize step boundaries")
 
 
+@pytest.mark.parametrize("q_per_seq", [3, 4])
+@pytest.mark.parametrize("fp8_keys", [False, True])
+def test_long_histories_with_three_and_four_tokens_per_sequence(q_per_seq, fp8_keys):
+    """Histories past the fused-select limit scored in runs of 3 or 4 tokens of
+    one sequence (the score pass then also builds each row's histogram), then
+    the collect and finalize launches; every selection against the oracle."""
+    _say(f"long histories, {q_per_seq} tokens per sequence, fp8={fp8_keys}")
+    from sparse_block_indexed_amd import ops
+    wl = I.make_workload(I.WorkloadSpec("long_runs", batch=2, seq_lens=[140000, 20000], q_per_seq=q_per_seq),
+                         seed=44, device="cuda")
+    pt, sl, qs, qp = device_tables(wl)
+    kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if fp8_keys else wl.k_idx_cache
+    sel = ops.indexer_topk(wl.q_idx, kidx, pt, sl, qs, qp, 512)
+    torch.cuda.synchronize()
+    _check_selection(wl, sel, range(wl.n_tok), kidx_fp8=kidx if fp8_keys else None,
+                     what=f"long runs of {q_per_seq}")
+
+
 def test_history_limits_of_the_select_paths():
     """Around the select paths' size limits, every selection checked against
     the oracle: a call whose longest history is exactly 16,384 blocks (scores
