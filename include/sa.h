@@ -29,6 +29,12 @@
  * - Results are deterministic: the same inputs and arguments give bitwise
  *   identical outputs, and a token's outputs do not depend on the other tokens
  *   of the call when num_splits is given explicitly.
+ * - Every call can be captured into a HIP graph: no call records a memset, an
+ *   allocation or a synchronisation (what must start at zero is cleared by a
+ *   kernel of the call itself).
+ * - The library keeps no global state. Calls on different streams may run at
+ *   the same time as long as they share no output buffer, partial-result
+ *   buffer or indexer workspace.
  * - All arrays are dense and row-major; device pointers must be 16-byte aligned.
  *
  * Cache layouts (this library's storage format; the pages fix none):
