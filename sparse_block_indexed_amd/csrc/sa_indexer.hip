@@ -452,8 +452,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
 // 16-byte fragment reads of 16 lanes hit 64 distinct banks). The page ids of
 // the workgroup's block range are read into LDS once per pass, so a tile's key
 // loads depend on no other global read; they are issued two tiles ahead (two
-// register sets), and one barrier per tile orders the LDS buffers. Rows of
-// another sequence than the one being processed are handled in further passes.
+// register sets), and one barrier per tile orders the LDS buffers. Each wave
+// passes its 16 x 32 scores through LDS and stores them as 16 bytes per lane (8
+// whole 128-byte row pieces per store). Rows of another sequence than the one
+// being processed are handled in further passes.
 constexpr int kGemmTokens = 64;
 constexpr int kGemmBlocks = 32;
 constexpr int kKeyStride = kKeyBytes + 16;
@@ -473,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
   constexpr int KB = KeyFmt<kFp8>::kBytes;
   __shared__ uint8_t s_keys[2][kGemmBlocks * kKeyStride];
   __shared__ int s_pages[kGemmPages];   // pass's pages, from its first tile on; -1 = unreadable
+  __shared__ float4 s_c[kThreads / 64][16][kGemmBlocks / 4 + 1];   // per wave: its 16 rows of a tile's scores
   __shared__ int s_tok_cb[kGemmTokens];
   __shared__ int s_tok_seq[kGemmTokens];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 15, lg = lane >> 4;
@@ -578,16 +581,28 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
           c[n] = mfma_bf16(qa[i], kb, c[n]);
         }
       }
-      // c[n][r]: token row 16*wave + 4*lg + r, block tile*kGemmBlocks + 16*n + lq
+      // c[n][r]: token row 16*wave + 4*lg + r, block tile*kGemmBlocks + 16*n + lq. The wave's 16 x 32
+      // scores go through LDS so that each store writes 16 bytes per lane, 8 whole rows of the tile
 #pragma unroll
       for (int n = 0; n < kSub; ++n) {
         const int beta = tile * kGemmBlocks + 16 * n + lq;
         const bool readable = beta < hi && s_pages[(min(beta, hi - 1) >> 3) - pg0] >= 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wave * 16 + 4 * lg + r;
-          if (((active >> row) & 1ull) && beta < s_tok_cb[row])
-            a.scores[(size_t)(t0 + row) * a.max_hist_blocks + beta] = readable ? c[n][r] : -INFINITY;
+        for (int r = 0; r < 4; ++r)
+          reinterpret_cast<float*>(&s_c[wave][4 * lg + r][0])[16 * n + lq] = readable ? c[n][r] : -INFINITY;
+      }
+      {
+        const int ch = lane & 7;
+        const int beta0 = tile * kGemmBlocks + 4 * ch;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rr = (lane >> 3) + 8 * h;
+          const int row = wave * 16 + rr;
+          const float4 v = s_c[wave][rr][ch];
+          // a store that starts inside the row's history may run up to 3 blocks past it: those scores
+          // are never read, and rows are a multiple of 8 blocks long, so it stays inside the row
+          if (((active >> row) & 1ull) && beta0 < s_tok_cb[row])
+            *reinterpret_cast<float4*>(&a.scores[(size_t)(t0 + row) * a.max_hist_blocks + beta0]) = v;
         }
       }
       if (tile + 1 < tl1) stash(buf ^ 1, next);
