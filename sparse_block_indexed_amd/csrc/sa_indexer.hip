@@ -114,21 +114,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
-// Exclusive prefix sum over the lanes of a wave of values below 2^NB, one
-// ballot per bit plane (no cross-lane moves); *total receives the wave's sum.
-template <int NB>
-__device__ __forceinline__ uint32_t wave_excl_scan_small(uint32_t c, uint32_t* total) {
-  uint32_t ex = 0, tot = 0;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const uint64_t m = __ballot((c >> b) & 1u);
-    ex += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
-    tot += (uint32_t)__popcll(m) << b;
-  }
-  *total = tot;
-  return ex;
-}
-
 // Exclusive suffix sum over the NT threads of the block: the sum of v over
 // threads with a larger index. s_tmp holds NT / 64 words.
 template <int NT>
