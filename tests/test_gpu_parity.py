@@ -296,6 +296,20 @@ def test_deterministic_and_batch_invariant():
         assert torch.equal(s1[0], s3[3]) and torch.equal(o1[0], o3[3]) and torch.equal(l1[0], l3[3])
 
 
+def test_sparse_layer_call_equals_its_two_steps():
+    """ops.sparse_layer (indexer top-k, then attention) gives bitwise what the
+    two binding calls give."""
+    _say("sparse_layer convenience call")
+    from sparse_block_indexed_amd import ops
+    wl = I.make_workload(SMALL, seed=14, device="cuda")
+    pt, sl, qs, qp = device_tables(wl)
+    sel, out, lse = ops.sparse_layer(wl.q, wl.q_idx, wl.k_cache, wl.v_cache, wl.k_idx_cache, pt, sl, qs, qp, SCALE,
+                                     num_splits=3)
+    sel2, out2, lse2 = run_sparse_layer(wl, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2) and torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 def test_split_count_changes_only_rounding():
     _say("splits")
     wl = I.named_workload("decode_8k_b1", device="cuda", seed=33)
