@@ -128,6 +128,16 @@ def test_long_history_step_graph_replays_match_eager():
     _graph_vs_eager(wl, 0)
 
 
+@pytest.mark.parametrize("q_per_seq", [20, 70])
+def test_mfma_scorer_steps_graph_replays_match_eager(q_per_seq):
+    """20 query tokens per sequence take the 16-row MFMA scorer and 70 the score
+    GEMM (and cacheable K/V loads); both under capture."""
+    _say(f"graph mfma scorers q_per_seq={q_per_seq}")
+    wl = I.make_workload(I.WorkloadSpec("mfma_graph", batch=2, seq_lens=[5000, 9000], q_per_seq=q_per_seq),
+                         seed=74, device="cuda")
+    _graph_vs_eager(wl, 0)
+
+
 def test_mtp_verify_step_graph_replays_match_eager():
     """The 128K MTP verify workload as the benchmark replays it."""
     _say("graph mtp_verify_128k_b64")
