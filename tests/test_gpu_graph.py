@@ -145,6 +145,33 @@ def test_mtp_verify_step_graph_replays_match_eager():
     _graph_vs_eager(wl, 0, replays=2)
 
 
+def test_calls_on_two_streams_at_once_match_eager():
+    """The library keeps no global state: two steps with their own buffers and
+    workspaces, enqueued on two streams (default priority) so that they can run
+    at the same time, give bitwise the results of running them one by one."""
+    _say("two streams")
+    wa = I.make_workload(SMALL, seed=75, device="cuda")
+    wb = I.make_workload(I.WorkloadSpec("long", batch=2, seq_lens=[200000, 30000], q_per_seq=2), seed=76,
+                         device="cuda")
+    sa, sb = _Step(wa, 3), _Step(wb, 0)
+    sa.run()
+    sb.run()
+    torch.cuda.synchronize()
+    ref_a = [t.clone() for t in sa.outputs()]
+    ref_b = [t.clone() for t in sb.outputs()]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for r in range(3):
+        sa.poison()
+        sb.poison()
+        torch.cuda.synchronize()
+        for st, step in zip(streams, (sa, sb)):
+            with torch.cuda.stream(st):
+                step.run()
+        torch.cuda.synchronize()
+        for got, want in zip(sa.outputs() + sb.outputs(), ref_a + ref_b):
+            assert torch.equal(got, want), f"round {r}"
+
+
 def test_hybrid_layer_group_graph():
     """Three window layers and one sparse layer, each with its own Q and caches
     over the same sequences, captured as one graph: every replay equals each
