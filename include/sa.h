@@ -79,7 +79,8 @@ typedef enum {
   SA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment */
   SA_ERR_UNSUPPORTED = 2,   /* a shape or constant outside what the kernels support */
   SA_ERR_WORKSPACE = 3,     /* workspace smaller than the *_workspace_size() answer */
-  SA_ERR_HIP = 4            /* a HIP launch error */
+  SA_ERR_HIP = 4,           /* a HIP launch error */
+  SA_STATUS_MAX_ENUM = 0x7FFFFFFF   /* not a status: keeps every int code a valid value of the type */
 } sa_status;
 
 /* One paged cache, shared by all calls of a layer.

@@ -107,6 +107,7 @@ const char* sa_status_string(sa_status s) {
     case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
     case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
     case SA_ERR_HIP: return "SA_ERR_HIP";
+    case SA_STATUS_MAX_ENUM: break;
   }
   return "SA_ERR_UNKNOWN";
 }
