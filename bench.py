@@ -70,10 +70,14 @@ def counter_traffic():
 def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: int = 64, kv_fp8=None,
                  q_groups=None, kidx_fp8=None):
     """The fp64 oracle timed on this host over a bounded sample of the same
-    workload: whole sequences' query tokens, until the budget is spent.
+    workload: whole sequences' query tokens (evenly spaced ones when a sequence
+    has more than max_tokens), until the budget is spent.
     kv_fp8 = (k_codes, v_codes, k_scale, v_scale) times the one-byte KV form,
     kidx_fp8 (E4M3 codes) the one-byte index keys, q_groups ([n_tok][4][256]
-    index queries) per-KV-group selection."""
+    index queries) per-KV-group selection.
+
+    Returns (baseline, refs): refs holds (token, selection or None, O, lse) of
+    every token the oracle ran, for the parity check of the timed buffers."""
     import torch
     from oracle import sa_oracle as O
     from sparse_block_indexed_amd import inputs as I
@@ -84,11 +88,14 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
         threads = 1
     done, t_cpu = 0, 0.0
     seqs_done = 0
+    refs = []
     dev = wl.k_cache.device
     for b in range(wl.batch):
-        toks = [t for t in range(wl.n_tok) if int(wl.q_seq[t]) == b][:max_tokens]
+        toks = [t for t in range(wl.n_tok) if int(wl.q_seq[t]) == b]
         if not toks:
             continue
+        if len(toks) > max_tokens:
+            toks = toks[::-(-len(toks) // max_tokens)]
         row = wl.page_table[b]
         # host copies of what the oracle reads (not timed): the sequence's index
         # keys and the pages of every attended block
@@ -122,17 +129,20 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
         for j, t in enumerate(toks):
             p = int(wl.q_pos[t])
             if window is not None:
-                O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.window_positions(p, window), SCALE,
-                                   fp8_scales=fp8_scales)
+                sel = None
+                o, l = O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.window_positions(p, window),
+                                          SCALE, fp8_scales=fp8_scales)
             elif q_groups is None:
                 keys = O.index_keys(kidx, np.arange(npg), p // 8, fp8=kidx_fp8 is not None)
                 sel = O.indexer_topk_token(O.bf16_to_f64(qib[j]), keys, 512)
-                O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.sparse_token_positions(sel, p), SCALE,
-                                   fp8_scales=fp8_scales)
+                o, l = O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.sparse_token_positions(sel, p),
+                                          SCALE, fp8_scales=fp8_scales)
             else:
                 keys = O.index_keys(kidx, np.arange(npg), p // 8, fp8=kidx_fp8 is not None)
-                sels = [O.indexer_topk_token(O.bf16_to_f64(qib[j][g]), keys, 512) for g in range(4)]
-                O.sparse_attention_token_grouped(qb[j], kc, vc, compact, sels, p, SCALE, fp8_scales=fp8_scales)
+                sel = np.stack([O.indexer_topk_token(O.bf16_to_f64(qib[j][g]), keys, 512) for g in range(4)])
+                o, l = O.sparse_attention_token_grouped(qb[j], kc, vc, compact, sel, p, SCALE,
+                                                        fp8_scales=fp8_scales)
+            refs.append((t, sel, o, l))
             done += 1
             if time.perf_counter() - t0 + t_cpu >= budget_s:
                 break
@@ -140,9 +150,35 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
         seqs_done += 1
         if t_cpu >= budget_s or done >= max_tokens:
             break
-    return {"value": done / t_cpu, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} query tokens ({seqs_done} sequences) of the {wl.spec.name} workload, fp64 numpy "
-                      f"oracle, {t_cpu:.1f} s of CPU time, host copies excluded"}
+    return ({"value": done / t_cpu, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+             "sample": f"{done} query tokens ({seqs_done} sequences) of the {wl.spec.name} workload, fp64 numpy "
+                       f"oracle, {t_cpu:.1f} s of CPU time, host copies excluded"}, refs)
+
+
+MAX_ABS, REL_RMS, LSE_ABS = 2e-2, 5e-3, 1e-3
+
+
+def parity_check(refs, sel_host, out, lse):
+    """The timed step's own buffers against the oracle's results for the same
+    tokens: selections bit for bit, outputs within max-abs 2e-2 and relative RMS
+    5e-3 over the compared tokens, lse within 1e-3."""
+    from oracle import sa_oracle as O
+    from sparse_block_indexed_amd import inputs as I
+    if not refs:
+        return {"tokens": 0, "pass": False}
+    toks = [r[0] for r in refs]
+    bad_sel = [t for t, sel, _, _ in refs if sel is not None and not np.array_equal(np.asarray(sel_host[t]), sel)]
+    got = O.bf16_to_f64(I.bf16_bits(out[toks]))
+    ref = np.stack([r[2] for r in refs])
+    err = np.abs(got - ref)
+    rel = float(np.sqrt((err ** 2).sum()) / max(np.sqrt((ref ** 2).sum()), 1e-300))
+    dl = float(np.abs(lse[toks].cpu().numpy().astype(np.float64) - np.stack([r[3] for r in refs])).max())
+    ok = (not bad_sel) and np.isfinite(got).all() and err.max() <= MAX_ABS and rel <= REL_RMS and dl <= LSE_ABS
+    return {"tokens": len(toks),
+            "selection": None if refs[0][1] is None else ("bit-exact" if not bad_sel else
+                                                          f"{len(bad_sel)} tokens differ"),
+            "max_abs": float(err.max()), "rel_rms": rel, "lse_max_abs": dl,
+            "tolerance": f"max-abs {MAX_ABS}, rel-RMS {REL_RMS}, lse {LSE_ABS}", "pass": bool(ok)}
 
 
 def capture(fn, reps: int = 1):
@@ -276,6 +312,12 @@ def layer_group(args, wl, dev):
              "indexer_topk": "sa_indexer_topk (score_kernel + select)",
              "sparse_decode": "attention_kernel<false, bf16>%s (sa_sparse_decode)" % (" + merge_kernel" if Ss > 1 else "")}
     group_bytes = sum(count[k] * nbytes[k] for k in nbytes)
+    # parity of the timed buffers: the first window layer and the sparse layer, a few tokens each
+    _, w_refs = cpu_baseline(layers[0], None, window, budget_s=2.0, max_tokens=4)
+    _, s_refs = cpu_baseline(wl, sel_host, None, budget_s=2.0, max_tokens=4)
+    parity = {"window_layer_0": parity_check(w_refs, None, outs[0], lses[0]),
+              "sparse_layer": parity_check(s_refs, sel_host, outs[3], lses[3])}
+    parity["pass"] = all(v["pass"] for v in parity.values())
     return {
         "metric": f"{name} hybrid layer group (3 window + 1 sparse layer) query-tokens/s; achieved HBM GB/s",
         "value": n_tok / (ms * 1e-3),
@@ -294,6 +336,7 @@ def layer_group(args, wl, dev):
         "algorithmic_bytes": {k: count[k] * nbytes[k] for k in nbytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": kname[dominant]},
+        "parity": parity,
     }
 
 
@@ -309,8 +352,9 @@ def main():
                     help="extra steps, each after a 1 GiB write that evicts L2/MALL (reported separately)")
     ap.add_argument("--workload", default=HEADLINE, choices=WORKLOAD_NAMES,
                     help="the workload (default: the headline %s)" % HEADLINE)
-    ap.add_argument("--num-splits", type=int, default=0,
-                    help="partitions per (token, group) for the attention call; 0 lets the library pick")
+    ap.add_argument("--num-splits", type=int, default=-1,
+                    help="partitions per (token, group) for the attention call: a count, 0 (each token's own "
+                         "length decides) or -1 (fill the GPU: the count follows the call's size)")
     ap.add_argument("--fp8-index-keys", action="store_true",
                     help="score one-byte (OCP E4M3) index keys: the same integer values, half the bytes")
     ap.add_argument("--fp8-kv", action="store_true",
@@ -354,7 +398,11 @@ def main():
     name = args.workload
     wl = I.named_workload(name, device=dev)
     if args.layer_group:
-        print(json.dumps(layer_group(args, wl, dev)), flush=True)
+        res = layer_group(args, wl, dev)
+        print(json.dumps(res), flush=True)
+        if not res["parity"]["pass"]:
+            print("parity check of the timed buffers FAILED", file=sys.stderr)
+            sys.exit(3)
         return
     pt, sl, qs, qp = wl.device_ints(dev)
     kidx = I.fp8_e4m3_codes(wl.k_idx_cache) if args.fp8_index_keys else wl.k_idx_cache
@@ -451,6 +499,9 @@ def main():
               "block_tokens": 8, "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S}
     config["kv_cache"] = "fp8_e4m3" if args.fp8_kv else "bf16"
     config["launch"] = "eager" if args.eager else "hip_graph"
+    config["num_splits_request"] = {-1: "fill_gpu", 0: "by_length"}.get(args.num_splits, args.num_splits)
+    # value: steps back to back with inputs resident in HBM and L2/MALL not flushed between steps
+    config["cache"] = "warm"
     if window is None:
         config["topk_blocks"] = topk
         config["index_keys"] = "fp8_e4m3" if args.fp8_index_keys else "bf16"
@@ -505,20 +556,31 @@ def main():
                               "traffic": counter_traffic() if (name == HEADLINE and not tags) else None,
                               "kernel": kname}
     if cold_ms is not None:
-        result["cold_cache"] = {"ms_per_step": cold_ms, "query_tokens_per_s": n_tok / (cold_ms * 1e-3)}
+        result["cold_cache"] = {"ms_per_step": cold_ms, "query_tokens_per_s": n_tok / (cold_ms * 1e-3),
+                                "how": "one-step graph replays timed with HIP events, each after a 1 GiB write "
+                                       "that evicts L2 and the 256 MB MALL"}
+    # The oracle leg: timed on the host as the CPU baseline, and its results
+    # compared with the buffers of the step just timed (outside the timed loop).
+    # With --no-cpu-baseline the oracle still runs a few tokens for the check.
+    import contextlib
+    limit = contextlib.nullcontext()
+    if args.cpu_threads > 0:   # cap the oracle's BLAS threads (e.g. 1 for a one-core figure)
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=args.cpu_threads)
+    with limit:
+        baseline, refs = cpu_baseline(wl, sel_host, window,
+                                      budget_s=2.0 if args.no_cpu_baseline else 20.0,
+                                      max_tokens=4 if args.no_cpu_baseline else 64,
+                                      kv_fp8=(kc, vc, kv_kw["k_scale"], kv_kw["v_scale"]) if args.fp8_kv else None,
+                                      q_groups=qidx if per_group else None,
+                                      kidx_fp8=kidx if args.fp8_index_keys else None)
     if not args.no_cpu_baseline:
-        import contextlib
-        limit = contextlib.nullcontext()
-        if args.cpu_threads > 0:   # cap the oracle's BLAS threads (e.g. 1 for a one-core figure)
-            from threadpoolctl import threadpool_limits
-            limit = threadpool_limits(limits=args.cpu_threads)
-        with limit:
-            result["cpu_baseline"] = cpu_baseline(wl, sel_host, window,
-                                                  kv_fp8=(kc, vc, kv_kw["k_scale"], kv_kw["v_scale"])
-                                                  if args.fp8_kv else None,
-                                                  q_groups=qidx if per_group else None,
-                                                  kidx_fp8=kidx if args.fp8_index_keys else None)
+        result["cpu_baseline"] = baseline
+    result["parity"] = parity_check(refs, sel_host, out, lse)
     print(json.dumps(result), flush=True)
+    if not result["parity"]["pass"]:
+        print("parity check of the timed buffers FAILED", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -28,7 +28,7 @@
  *   (p < 8) selects nothing and attends its own block only.
  * - Results are deterministic: the same inputs and arguments give bitwise
  *   identical outputs, and a token's outputs do not depend on the other tokens
- *   of the call when num_splits is given explicitly.
+ *   of the call unless num_splits is SA_SPLITS_FILL_GPU.
  * - Every call can be captured into a HIP graph: no call records a memset, an
  *   allocation or a synchronisation (what must start at zero is cleared by a
  *   kernel of the call itself).
@@ -69,6 +69,23 @@ extern "C" {
 #define SA_MAX_TOPK 512
 #define SA_MAX_WINDOW 4096
 #define SA_MAX_SPLITS 64
+
+/* Partition requests for the num_splits argument of the decode calls. A
+ * decode call cuts each (token, KV group)'s attended blocks into partitions
+ * whose partial results are merged (SGLang blog, "Kernels from StepFun"):
+ *   n > 0                n partitions for every token (at most SA_MAX_SPLITS);
+ *   SA_SPLITS_BY_LENGTH  each token's count follows its own attended length
+ *                        only: ceil(blocks / SA_SPLIT_BLOCKS) partitions, so a
+ *                        token's results never depend on the other tokens of
+ *                        the call (the GB300 bring-up, "MTP: the free win and
+ *                        the not-quite-free one", records the hazard of verify
+ *                        tokens taking a numerically different path);
+ *   SA_SPLITS_FILL_GPU   the count follows the size of the call so that the
+ *                        grid fills the GPU: fastest, but a token's bits may
+ *                        change with the batch it is part of. */
+#define SA_SPLITS_BY_LENGTH 0
+#define SA_SPLITS_FILL_GPU (-1)
+#define SA_SPLIT_BLOCKS 128
 
 /* Storage formats of a cache (index keys or K/V) for the entry points that take one. */
 #define SA_FORMAT_BF16 0
@@ -168,9 +185,18 @@ sa_status sa_indexer_topk_grouped(const void* q_idx, const void* k_idx_cache, in
                                   int n_tok, int topk, int32_t* sel_idx, void* workspace,
                                   size_t ws_bytes, hipStream_t stream);
 
-/* Number of partitions a decode call uses for a given request
- * (num_splits > 0 is returned clamped to SA_MAX_SPLITS; 0 picks from n_tok and
- * max_blocks_per_token so that the grid fills the GPU). */
+/* Partition extent S of a decode call's partial-result buffers for a request
+ * (the S of part_o [n_tok][S][64][192]); max_blocks_per_token is the longest
+ * attended list a token of the call can have (topk + 1 for the sparse layer,
+ * window / 8 + 2 for the window layer).
+ *   num_splits > 0       -> min(num_splits, SA_MAX_SPLITS)
+ *   SA_SPLITS_BY_LENGTH  -> ceil(max_blocks_per_token / SA_SPLIT_BLOCKS); a token
+ *                           with a shorter list uses its own, smaller count and
+ *                           leaves its further partitions empty (lse = -inf)
+ *   SA_SPLITS_FILL_GPU   -> partitions raised until the grid holds about one
+ *                           workgroup per CU, keeping every wave of a workgroup at
+ *                           least one 4-block chunk
+ * Another negative value returns 1. */
 int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits);
 
 /*
@@ -185,9 +211,12 @@ int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits);
  * q            device bf16 [n_tok][64][192]
  * k_cache, v_cache  device bf16, layouts above
  * sel_idx      device int32 [n_tok][topk] (as written by sa_indexer_topk)
- * num_splits   partitions per (token, group); 0 = sa_resolve_num_splits(n_tok, topk + 1, 0)
+ * num_splits   partitions per (token, group): n > 0, SA_SPLITS_BY_LENGTH or
+ *              SA_SPLITS_FILL_GPU (above); S = sa_resolve_num_splits(n_tok,
+ *              topk + 1, num_splits); below SA_SPLITS_FILL_GPU is SA_ERR_INVALID_ARG
  * part_o, part_lse  device fp32 [n_tok][S][64][192], [n_tok][S][64]; needed when
- *              the resolved S > 1, ignored (may be NULL) when S == 1
+ *              S > 1, ignored (may be NULL) when S == 1. A partition with
+ *              lse = -inf attended nothing and its part_o may hold anything
  * out          device bf16 [n_tok][64][192] (round to nearest even) or NULL;
  *              when S > 1 and out is non-NULL the merge is enqueued too, when
  *              out is NULL only the partitions are written
@@ -221,8 +250,8 @@ sa_status sa_sparse_decode_grouped(const void* q, const void* k_cache, const voi
  * Sliding-window GQA attention: token t at position p attends positions
  * max(0, p - window + 1) .. p. (SGLang blog, "Hybrid Attention": three of
  * every four layers read the latest 512 tokens.) Arguments as sa_sparse_decode;
- * window 1 .. SA_MAX_WINDOW; num_splits 0 = sa_resolve_num_splits(n_tok,
- * window / 8 + 2, 0).
+ * window 1 .. SA_MAX_WINDOW; S = sa_resolve_num_splits(n_tok, window / 8 + 2,
+ * num_splits).
  */
 sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
                         sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
@@ -260,8 +289,9 @@ sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void
 /*
  * Merge of per-partition results (SGLang blog, "Kernels from StepFun").
  * With M = max_s lse_s: O = sum_s e^(lse_s - M) O_s / sum_s e^(lse_s - M),
- * lse = M + ln sum_s e^(lse_s - M). Partitions with lse = -inf carry no weight;
- * if all are empty the output is 0 and lse = -inf.
+ * lse = M + ln sum_s e^(lse_s - M). Partitions with lse = -inf carry no weight
+ * and their part_o is not used (it may hold anything, NaN included); if all are
+ * empty the output is 0 and lse = -inf.
  * part_o device fp32 [n_tok][num_splits][num_heads][head_dim]; part_lse
  * [n_tok][num_splits][num_heads]; out device bf16 [n_tok][num_heads][head_dim];
  * out_lse fp32 [n_tok][num_heads] or NULL. head_dim must be a multiple of 4

@@ -263,19 +263,21 @@ def merge(part_o: np.ndarray, part_lse: np.ndarray):
     """Combine per-partition (O, lse) into the result over the union of partitions.
 
     part_o: [S][heads][dim] normalised partial outputs; part_lse: [S][heads].
-    Partitions with lse = -inf (nothing attended) carry no weight.
+    Partitions with lse = -inf (nothing attended) carry no weight: they are left
+    out of the sum, so whatever their part_o holds does not matter.
     """
     part_o = np.asarray(part_o, dtype=np.float64)
     part_lse = np.asarray(part_lse, dtype=np.float64)
-    M = part_lse.max(axis=0)
     out = np.zeros(part_o.shape[1:], dtype=np.float64)
     lse = np.full(part_lse.shape[1], -np.inf)
     for h in range(part_lse.shape[1]):
-        if not np.isfinite(M[h]):
+        live = np.isfinite(part_lse[:, h])
+        if not live.any():
             continue
-        w = np.exp(part_lse[:, h] - M[h])
-        out[h] = (w[:, None] * part_o[:, h, :]).sum(axis=0) / w.sum()
-        lse[h] = M[h] + np.log(w.sum())
+        M = part_lse[live, h].max()
+        w = np.exp(part_lse[live, h] - M)
+        out[h] = (w[:, None] * part_o[live, h, :]).sum(axis=0) / w.sum()
+        lse[h] = M + np.log(w.sum())
     return out, lse
 
 

@@ -36,7 +36,7 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
                         int max_blocks, int num_splits, float* part_o, float* part_lse, void* out,
                         float* out_lse, bool window_mode, const int32_t* sel_idx, int topk, int window,
                         bool kv_fp8, float k_scale, float v_scale, bool sel_per_group, hipStream_t stream) {
-  if (n_tok < 0 || num_splits < 0) return SA_ERR_INVALID_ARG;
+  if (n_tok < 0 || num_splits < SA_SPLITS_FILL_GPU) return SA_ERR_INVALID_ARG;
   if (n_tok == 0) return SA_OK;
   if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return SA_ERR_INVALID_ARG;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr) return SA_ERR_INVALID_ARG;
@@ -71,6 +71,8 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   a.topk = topk;
   a.window = window;
   a.num_splits = S;
+  // by length: a token with a shorter list than the longest uses fewer partitions
+  a.split_blocks = num_splits == SA_SPLITS_BY_LENGTH ? SA_SPLIT_BLOCKS : 0;
   a.batch = pd.batch;
   a.max_pages = pd.max_pages_per_seq;
   a.num_pages = pd.num_pages;
@@ -120,6 +122,10 @@ size_t sa_indexer_topk_workspace_size(int n_tok, int max_pages_per_seq, int topk
 
 int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits) {
   if (num_splits > 0) return std::min(num_splits, SA_MAX_SPLITS);
+  if (num_splits == SA_SPLITS_BY_LENGTH)   // the longest list's own count (the kernel gives each token its own)
+    return std::max(1, std::min((std::max(1, max_blocks_per_token) + SA_SPLIT_BLOCKS - 1) / SA_SPLIT_BLOCKS,
+                                SA_MAX_SPLITS));
+  if (num_splits != SA_SPLITS_FILL_GPU) return 1;
   // Reach about one workgroup per CU while giving every wave of a workgroup at
   // least one 4-block chunk: a chunk costs about one memory round trip when
   // few workgroups run, so tiny grids want short partitions (a one-token

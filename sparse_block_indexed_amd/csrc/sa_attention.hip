@@ -166,9 +166,14 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       nslots = nsel + 1;
     }
   }
+  // This token's own partition count: S, or (split by length) the count its
+  // own list length asks for, so that its partition boundaries do not depend
+  // on the longest list of the call; its further partitions stay empty.
+  const int St = a.split_blocks > 0 ? min(S, max(1, (nslots + a.split_blocks - 1) / a.split_blocks)) : S;
+  const bool live = sp < St;
   // sp * nslots < 64 * 514: 32-bit division
-  const int s0 = (int)((unsigned)(sp * nslots) / (unsigned)S);
-  const int s1 = (int)((unsigned)((sp + 1) * nslots) / (unsigned)S);
+  const int s0 = live ? (int)((unsigned)(sp * nslots) / (unsigned)St) : 0;
+  const int s1 = live ? (int)((unsigned)((sp + 1) * nslots) / (unsigned)St) : 0;
   const int n_all = s1 - s0;
 
   // Slot table: every thread issues all of its block-id loads, then all of its

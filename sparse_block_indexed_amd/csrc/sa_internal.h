@@ -39,7 +39,8 @@ struct AttnArgs {
   int n_tok;
   int topk;                 // sparse mode
   int window;               // window mode
-  int num_splits;
+  int num_splits;           // partition extent S of the partial buffers
+  int split_blocks;         // > 0: a token uses min(S, ceil(its blocks / split_blocks)) partitions
   int batch;
   int max_pages;
   int num_pages;

@@ -90,8 +90,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(s0 + u, 63)));
+        // a partition with no weight (empty, or past S) adds nothing: a select,
+        // not a product, so that whatever its slot holds (NaN included) stays out
         const float wgt = s0 + u < S ? wu : 0.f;
-        acc += v[u] * wgt;
+        acc = wgt != 0.f ? acc + v[u] * wgt : acc;
       }
     }
     if (d4b + lane < q4) {

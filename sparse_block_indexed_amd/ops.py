@@ -26,6 +26,10 @@ EXPORTED = ["sa_status_string", "sa_indexer_topk_workspace_size", "sa_indexer_to
             "sa_swa_decode_fp8kv", "sa_merge", "sa_indexer_topk_grouped_workspace_size",
             "sa_indexer_topk_grouped", "sa_sparse_decode_grouped"]
 FORMAT_BF16, FORMAT_FP8_E4M3 = 0, 1
+# num_splits requests (besides a count n > 0): each token's partition count
+# follows its own attended length only (batch invariant), or the call's size so
+# that the grid fills the GPU
+SPLITS_BY_LENGTH, SPLITS_FILL_GPU = 0, -1
 
 
 class SAError(RuntimeError):

@@ -132,9 +132,18 @@ int main() {
   expect(sa_merge(PF, PF, 1 << 20, 2, 64, 192, P, nullptr, nullptr), SA_ERR_UNSUPPORTED, "merge grid limit");
 
   // split policy and status names
-  expect(sa_resolve_num_splits(1, 513, 0), 32, "one 8K token: 32 partitions");
-  expect(sa_resolve_num_splits(256, 513, 0), 1, "the 128K verify batch: unsplit");
+  expect(sa_resolve_num_splits(1, 513, SA_SPLITS_FILL_GPU), 32, "fill the GPU: one 8K token, 32 partitions");
+  expect(sa_resolve_num_splits(256, 513, SA_SPLITS_FILL_GPU), 1, "fill the GPU: the 128K verify batch unsplit");
+  expect(sa_resolve_num_splits(1, 513, SA_SPLITS_BY_LENGTH), 5, "by length: 513 blocks, 5 partitions");
+  expect(sa_resolve_num_splits(256, 513, SA_SPLITS_BY_LENGTH), 5, "by length: the same for any batch");
+  expect(sa_resolve_num_splits(64, 66, SA_SPLITS_BY_LENGTH), 1, "by length: a 512 window, unsplit");
+  expect(sa_resolve_num_splits(1, 1 << 20, SA_SPLITS_BY_LENGTH), SA_MAX_SPLITS, "by length: clamped");
   expect(sa_resolve_num_splits(4, 513, 100), SA_MAX_SPLITS, "explicit count clamped");
+  expect(sa_resolve_num_splits(4, 513, -7), 1, "another negative request");
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, -2, nullptr, nullptr, P, nullptr, nullptr),
+         SA_ERR_INVALID_ARG, "sparse num_splits -2");
+  expect(sa_swa_decode(P, P, P, d, PI, PI, 2, 512, 0.1f, -2, nullptr, nullptr, P, nullptr, nullptr),
+         SA_ERR_INVALID_ARG, "window num_splits -2");
   expect(strcmp(sa_status_string((sa_status)99), "SA_ERR_UNKNOWN") == 0, 1, "unknown status name");
 
   printf("%d checks, %d failed\n%s\n", g_checks, g_failures,

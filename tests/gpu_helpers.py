@@ -12,6 +12,8 @@ from oracle import sa_oracle as O
 from sparse_block_indexed_amd import inputs as I
 
 SCALE = 1.0 / math.sqrt(192.0)
+SPLITS_BY_LENGTH = 0       # a token's partition count follows its own list length (batch invariant)
+SPLITS_FILL_GPU = -1       # the count follows the call's size (the benchmark's launch configuration)
 MAX_ABS = 2e-2
 REL_RMS = 5e-3
 LSE_ABS = 1e-3

@@ -60,15 +60,25 @@ def test_workspace_size(lib):
 
 def test_resolve_num_splits(lib):
     r = lib.sa_resolve_num_splits
-    assert r(256, 513, 0) == 1          # 128K verify batch: the grid already fills the GPU
-    assert r(1, 513, 0) == 32           # one token: 129 chunks over 32 partitions (1 chunk per wave)
-    assert r(64, 66, 0) == 1            # sliding window, batch 64: one workgroup per (token, group)
-    assert r(4, 513, 0) == 16
-    assert r(16, 513, 0) == 4           # the grid reaches 256 workgroups first
-    assert r(1, 66, 0) == 4             # one-token window: 17 chunks
-    assert r(1, 1, 0) == 1              # nothing to split
+    fill, by_len = -1, 0
+    # fill the GPU: follows the call's size
+    assert r(256, 513, fill) == 1       # 128K verify batch: the grid already fills the GPU
+    assert r(1, 513, fill) == 32        # one token: 129 chunks over 32 partitions (1 chunk per wave)
+    assert r(64, 66, fill) == 1         # sliding window, batch 64: one workgroup per (token, group)
+    assert r(4, 513, fill) == 16
+    assert r(16, 513, fill) == 4        # the grid reaches 256 workgroups first
+    assert r(1, 66, fill) == 4          # one-token window: 17 chunks
+    assert r(1, 1, fill) == 1           # nothing to split
+    # by length: one partition per 128 blocks of the longest list, whatever the call's size
+    for n in (1, 4, 64, 256, 100000):
+        assert r(n, 513, by_len) == 5
+        assert r(n, 66, by_len) == 1
+        assert r(n, 514, by_len) == 5
+        assert r(n, 4096 // 8 + 2, by_len) == 5
+    assert r(1, 128, by_len) == 1 and r(1, 129, by_len) == 2
     assert r(3, 513, 7) == 7            # explicit value kept
     assert r(3, 513, 1000) == 64        # clamped
+    assert r(3, 513, -5) == 1           # not a request: one partition
 
 
 def _desc(ops, batch=1, max_pages=16, num_pages=16, pt=0x1000, sl=0x2000):

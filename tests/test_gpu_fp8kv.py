@@ -13,7 +13,8 @@ import torch
 
 from sparse_block_indexed_amd import inputs as I
 
-from gpu_helpers import SCALE, OracleView, assert_close_outputs, bf16_to_np, device_tables, run_sparse_layer, run_swa
+from gpu_helpers import (SCALE, SPLITS_FILL_GPU, OracleView, assert_close_outputs, bf16_to_np, device_tables,
+                         run_sparse_layer, run_swa)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,7 @@ SMALL = I.WorkloadSpec("small_mixed", batch=12,
                        q_per_seq=3, spare_pages=5)
 
 
-@pytest.mark.parametrize("num_splits", [0, 1, 3])
+@pytest.mark.parametrize("num_splits", [0, -1, 1, 3])
 def test_fp8kv_small_mixed_sparse(num_splits):
     _say(f"fp8kv small_mixed sparse S={num_splits}")
     wl = I.make_workload(SMALL, seed=61, device="cuda")
@@ -91,22 +92,20 @@ def test_fp8kv_small_mixed_swa(window, num_splits):
 
 
 def test_fp8kv_mtp_verify_128k_b64():
-    """The headline workload at full size, default launch configuration;
-    attention on a sample of 16 tokens."""
+    """The headline workload at full size in the benchmark's launch
+    configuration: every token's selection and output."""
     _say("fp8kv mtp_verify_128k_b64")
     wl = I.named_workload("mtp_verify_128k_b64", device="cuda")
     kv = _quantize(wl)
-    sel, out, lse = run_sparse_layer(wl, kv_fp8=kv)
-    rng = np.random.default_rng(0)
-    sample = sorted(rng.choice(wl.n_tok, size=16, replace=False).tolist())
-    _check_sparse(wl, kv, sel, out, lse, sample, what="fp8kv mtp_verify_128k")
+    sel, out, lse = run_sparse_layer(wl, kv_fp8=kv, num_splits=SPLITS_FILL_GPU)
+    _check_sparse(wl, kv, sel, out, lse, range(wl.n_tok), what="fp8kv mtp_verify_128k")
 
 
 def test_fp8kv_swa_decode_32k_b64():
     _say("fp8kv swa_decode_32k_b64")
     wl = I.named_workload("swa_decode_32k_b64", device="cuda")
     kv = _quantize(wl)
-    out, lse = run_swa(wl, kv_fp8=kv)
+    out, lse = run_swa(wl, kv_fp8=kv, num_splits=SPLITS_FILL_GPU)
     ov = OracleView(wl, kv_fp8=kv)
     refs = [ov.swa(t) for t in range(wl.n_tok)]
     assert_close_outputs(bf16_to_np(out), lse.cpu().numpy(), np.stack([r[0] for r in refs]),

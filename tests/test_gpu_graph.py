@@ -113,7 +113,7 @@ SMALL = I.WorkloadSpec("small_mixed", batch=12,
                        q_per_seq=3, spare_pages=5)
 
 
-@pytest.mark.parametrize("num_splits,fp8_kv", [(1, False), (3, False), (0, True)])
+@pytest.mark.parametrize("num_splits,fp8_kv", [(1, False), (3, False), (0, True), (0, False), (-1, False)])
 def test_small_step_graph_replays_match_eager(num_splits, fp8_kv):
     _say(f"graph small S={num_splits} fp8_kv={fp8_kv}")
     wl = I.make_workload(SMALL, seed=71, device="cuda")
@@ -142,7 +142,7 @@ def test_mtp_verify_step_graph_replays_match_eager():
     """The 128K MTP verify workload as the benchmark replays it."""
     _say("graph mtp_verify_128k_b64")
     wl = I.named_workload("mtp_verify_128k_b64", device="cuda")
-    _graph_vs_eager(wl, 0, replays=2)
+    _graph_vs_eager(wl, -1, replays=2)
 
 
 def test_calls_on_two_streams_at_once_match_eager():

@@ -59,7 +59,7 @@ SMALL = I.WorkloadSpec("small_mixed", batch=12,
                        q_per_seq=3, spare_pages=5)
 
 
-@pytest.mark.parametrize("num_splits", [0, 1, 3])
+@pytest.mark.parametrize("num_splits", [0, -1, 1, 3])
 def test_grouped_small_mixed(num_splits):
     _say(f"grouped small S={num_splits}")
     wl = I.make_workload(SMALL, seed=91, device="cuda")

@@ -30,6 +30,7 @@ PINS = [
     (P.test_attention_closed_forms, {}),
     (P.test_merge_single_partition_identity, {}),
     (P.test_merge_all_empty, {}),
+    (P.test_merge_ignores_whatever_an_empty_partition_holds, {}),
     (P.test_merge_of_split_equals_unsplit, {"splits": 3}),
     (P.test_fp8_e4m3_hand_values, {}),
     (P.test_topk_brute_force, {"seed": 0}),
@@ -102,6 +103,24 @@ def _merge_without_empty_rule(part_o, part_lse):
         return (w[:, :, None] * part_o).sum(axis=0) / w.sum(axis=0)[:, None], M + np.log(w.sum(axis=0))
 
 
+def _merge_zero_weight_product(part_o, part_lse):
+    # empty partitions weighted by a product with 0 instead of being left out
+    part_o = np.asarray(part_o, dtype=np.float64)
+    part_lse = np.asarray(part_lse, dtype=np.float64)
+    out = np.zeros(part_o.shape[1:])
+    lse = np.full(part_lse.shape[1], -np.inf)
+    for h in range(part_lse.shape[1]):
+        live = np.isfinite(part_lse[:, h])
+        if not live.any():
+            continue
+        M = part_lse[live, h].max()
+        w = np.exp(part_lse[:, h] - M)
+        with np.errstate(invalid="ignore"):
+            out[h] = (w[:, None] * part_o[:, h, :]).sum(axis=0) / w.sum()
+        lse[h] = M + np.log(w.sum())
+    return out, lse
+
+
 def _attend_base2_lse(q, ks, vs, scale):
     o, lse = ORIG["attend"](q, ks, vs, scale)
     return o, lse / math.log(2.0)
@@ -151,6 +170,7 @@ MUTATIONS = {
     "the window holds one token too many": ("window_positions", _window_one_too_many),
     "the merge is not normalised": ("merge", _merge_unnormalised),
     "the merge gives empty partitions weight": ("merge", _merge_without_empty_rule),
+    "the merge multiplies empty partitions by zero": ("merge", _merge_zero_weight_product),
     "K is read through the V layout": ("k_rows", ORIG["v_rows"]),
     "lse is in base 2": ("attend", _attend_base2_lse),
     "the softmax scale is ignored": ("attend", _attend_unscaled),

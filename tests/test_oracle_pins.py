@@ -337,6 +337,22 @@ def test_merge_all_empty():
     assert (mo == 0).all() and np.isneginf(ml).all()
 
 
+def test_merge_ignores_whatever_an_empty_partition_holds():
+    """An empty partition carries no weight (SGLang blog, "Kernels from
+    StepFun": only attended partitions enter the merge): NaN or inf in its
+    slot changes nothing, bit for bit, against the merge without it."""
+    rng = np.random.default_rng(3)
+    po = rng.standard_normal((3, 64, 192))
+    pl = rng.standard_normal((3, 64)) * 2
+    ref_o, ref_l = O.merge(po, pl)
+    for junk in (np.nan, np.inf, -np.inf):
+        po2 = np.concatenate([po[:1], np.full((1, 64, 192), junk), po[1:]])
+        pl2 = np.concatenate([pl[:1], np.full((1, 64), -np.inf), pl[1:]])
+        mo, ml = O.merge(po2, pl2)
+        np.testing.assert_array_equal(mo, ref_o)
+        np.testing.assert_array_equal(ml, ref_l)
+
+
 # ---------------------------------------------------------------------------
 # One-byte index keys: OCP FP8 E4M3 decoding
 # ---------------------------------------------------------------------------
