@@ -150,6 +150,10 @@ def assert_close_outputs(got_out, got_lse, ref_out, ref_lse, what=""):
     assert err.max() <= MAX_ABS, f"{what}: max abs {err.max():.3e}"
     assert rel <= REL_RMS, f"{what}: rel rms {rel:.3e}"
     if got_lse is not None:
-        dl = np.abs(np.asarray(got_lse, dtype=np.float64) - np.asarray(ref_lse, dtype=np.float64))
-        assert dl.max() <= LSE_ABS, f"{what}: lse max abs {dl.max():.3e}"
+        gl = np.asarray(got_lse, dtype=np.float64)
+        rl = np.asarray(ref_lse, dtype=np.float64)
+        same = gl == rl                      # equal infinities (heads that attended nothing) count as equal
+        with np.errstate(invalid="ignore"):
+            dl = np.where(same, 0.0, np.abs(gl - rl))
+        assert not np.isnan(dl).any() and dl.max() <= LSE_ABS, f"{what}: lse max abs {dl.max():.3e}"
     return err.max(), rel
