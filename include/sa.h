@@ -185,6 +185,23 @@ sa_status sa_indexer_topk_grouped(const void* q_idx, const void* k_idx_cache, in
                                   int n_tok, int topk, int32_t* sel_idx, void* workspace,
                                   size_t ws_bytes, hipStream_t stream);
 
+/*
+ * sa_indexer_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The workspace is a device array inside the library, SA_NOALLOC_SCRATCH_BYTES
+ * long, one per GPU the library runs on (held until the process ends); the
+ * call allocates nothing. Every other argument and the result are those of
+ * sa_indexer_topk. Sizes whose workspace (sa_indexer_topk_workspace_size) is
+ * larger than the array give SA_ERR_WORKSPACE (the 128K verify batch, 256 tokens
+ * of 131,072-token histories, needs 26 MiB). All calls on one GPU share the
+ * array: calls that overlap on one GPU (other streams, other threads) race.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+sa_status sa_indexer_topk_noalloc(const void* q_idx, const void* k_idx_cache, sa_paged_desc pd,
+                                  const int32_t* q_seq, const int32_t* q_pos, int n_tok, int topk,
+                                  int32_t* sel_idx, hipStream_t stream);
+
 /* Partition extent S of a decode call's partial-result buffers for a request
  * (the S of part_o [n_tok][S][64][192]); max_blocks_per_token is the longest
  * attended list a token of the call can have (topk + 1 for the sparse layer,

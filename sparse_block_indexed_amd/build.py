@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsa.so")
-SOURCES = ["sa_api.cpp", "sa_attention.hip", "sa_indexer.hip", "sa_merge.hip"]
+SOURCES = ["sa_api.cpp", "sa_attention.hip", "sa_indexer.hip", "sa_merge.hip", "sa_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

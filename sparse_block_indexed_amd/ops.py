@@ -24,7 +24,7 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = ra
 EXPORTED = ["sa_status_string", "sa_indexer_topk_workspace_size", "sa_indexer_topk", "sa_indexer_topk_fp8",
             "sa_resolve_num_splits", "sa_sparse_decode", "sa_sparse_decode_fp8kv", "sa_swa_decode",
             "sa_swa_decode_fp8kv", "sa_merge", "sa_indexer_topk_grouped_workspace_size",
-            "sa_indexer_topk_grouped", "sa_sparse_decode_grouped"]
+            "sa_indexer_topk_grouped", "sa_sparse_decode_grouped", "sa_indexer_topk_noalloc"]
 FORMAT_BF16, FORMAT_FP8_E4M3 = 0, 1
 # num_splits requests (besides a count n > 0): each token's partition count
 # follows its own attended length only (batch invariant), or the call's size so
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sa_sparse_decode_grouped.restype = i32
     lib.sa_sparse_decode_grouped.argtypes = [vp, vp, vp, i32, f32, f32, PagedDesc, vp, vp, vp, i32, i32, f32, i32,
                                              vp, vp, vp, vp, vp]
+    lib.sa_indexer_topk_noalloc.restype = i32
+    lib.sa_indexer_topk_noalloc.argtypes = [vp, vp, PagedDesc, vp, vp, i32, i32, vp, vp]
     lib.sa_merge.restype = i32
     lib.sa_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     _lib = lib
@@ -171,6 +173,33 @@ def indexer_topk(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk: i
         name = "sa_indexer_topk_fp8" if fp8 else "sa_indexer_topk"
         st = getattr(lib, name)(_ptr(q_idx), _ptr(k_idx_cache), *tail)
     _check(name, st)
+    return sel_idx
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SA_NOALLOC_SCRATCH_BYTES
+
+
+def indexer_topk_noalloc(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk: int = MAX_TOPK,
+                         sel_idx=None, stream=None):
+    """sa_indexer_topk_noalloc: the bf16-key selection with the library's own
+    per-GPU scratch array as workspace (no workspace argument). Pass sel_idx to
+    allocate nothing at all; calls that overlap on one GPU race."""
+    lib = load_library()
+    dev = q_idx.device
+    n_tok = q_idx.shape[0]
+    _need(q_idx, "q_idx", torch.bfloat16, dev, (n_tok, DI))
+    _need(k_idx_cache, "k_idx_cache", torch.bfloat16, dev)
+    if k_idx_cache.dim() != 3 or tuple(k_idx_cache.shape[1:]) != (8, DI):
+        raise ValueError("k_idx_cache: expected [num_pages][8][256]")
+    _need(q_seq, "q_seq", torch.int32, dev, (n_tok,))
+    _need(q_pos, "q_pos", torch.int32, dev, (n_tok,))
+    pd = _desc(page_table, seq_lens, k_idx_cache.shape[0])
+    if sel_idx is None:
+        sel_idx = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, dev, (n_tok, topk))
+    st = lib.sa_indexer_topk_noalloc(_ptr(q_idx), _ptr(k_idx_cache), pd, _ptr(q_seq), _ptr(q_pos), n_tok, topk,
+                                     _ptr(sel_idx), _stream(stream))
+    _check("sa_indexer_topk_noalloc", st)
     return sel_idx
 
 

@@ -43,7 +43,8 @@ def build(verbose: bool = False) -> str:
     val_o = os.path.join(OBJ, "c_abi_validation.o")
     _run(common + san + ["-c", os.path.join(pkg, "csrc", "sa_api.cpp"), "-o", api_o], verbose)
     _run(common + san + ["-c", VAL_SRC, "-o", val_o], verbose)
-    kernels = [os.path.join(pkg, "_build", f + ".o") for f in ("sa_attention.hip", "sa_indexer.hip", "sa_merge.hip")]
+    kernels = [os.path.join(pkg, "_build", f + ".o")
+               for f in ("sa_attention.hip", "sa_indexer.hip", "sa_merge.hip", "sa_noalloc.hip")]
     _run([HIPCC, "--offload-arch=gfx950", "-fno-gpu-sanitize", "-fsanitize=address", "-fsanitize=undefined", val_o, api_o] + kernels + ["-o", VAL_EXE], verbose)
     return EXE
 

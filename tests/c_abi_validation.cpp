@@ -68,6 +68,18 @@ int main() {
   expect(sa_indexer_topk_fp8(P, P, d, PI, PI, 4, 512, PI, P, ws - 1, nullptr), SA_ERR_WORKSPACE,
          "fp8 indexer short ws");
 
+  // the indexer with the library's own scratch (refused before any HIP call)
+  expect(sa_indexer_topk_noalloc(nullptr, nullptr, d, nullptr, nullptr, 0, 512, nullptr, nullptr), SA_OK,
+         "no-alloc indexer n_tok 0");
+  expect(sa_indexer_topk_noalloc(nullptr, P, d, PI, PI, 4, 512, PI, nullptr), SA_ERR_INVALID_ARG,
+         "no-alloc indexer null q");
+  expect(sa_indexer_topk_noalloc(P, P, d, PI, PI, -3, 512, PI, nullptr), SA_ERR_INVALID_ARG,
+         "no-alloc indexer n_tok -3");
+  expect(sa_indexer_topk_noalloc(P, P, desc(64, 2048, 1 << 20), PI, PI, 1024, 512, PI, nullptr), SA_ERR_WORKSPACE,
+         "no-alloc indexer: 1024 tokens of 128K histories need more than the scratch array");
+  expect(sa_indexer_topk_workspace_size(256, 2048, 512) <= SA_NOALLOC_SCRATCH_BYTES, 1,
+         "the 128K verify batch fits the scratch array");
+
   // per-group indexer
   const size_t gws = sa_indexer_topk_grouped_workspace_size(4, 16, 512);
   expect(gws == sa_indexer_topk_workspace_size(16, 16, 512), 1, "grouped workspace covers 4 rows per token");
