@@ -190,20 +190,20 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   // 16-row MFMA scorer keeps one key tile in flight per wave and fits three
   // waves per SIMD: it wants about four workgroups per CU.
   const long long target_wgs = a.use_mfma16 ? 1024 : 512;
-  int chunk = 4096;
+  // the per-token scorer keeps its chunk of every row in LDS: at most kCandChunkMax blocks
+  int chunk = a.use_mfma16 ? 4096 : sa::kCandChunkMax;
   while (chunk > 64 && (long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) < target_wgs) chunk >>= 1;
   a.chunk_blocks = chunk;
-  // launch limits of the score and collect grids (256 threads per workgroup)
+  // launch limit of the score grid (256 threads per workgroup)
   if ((long long)ngroups * ((a.max_hist_blocks + chunk - 1) / chunk) * 256 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;
-  if (a.max_hist_blocks > sa::kFuseLimit &&
-      (long long)n_rows * ((a.max_hist_blocks + sa::kCollectChunk - 1) / sa::kCollectChunk) * 256 >= kMaxGridThreads)
-    return SA_ERR_UNSUPPORTED;
-  a.bitmap_words = a.max_hist_blocks <= sa::kBitmapMaxBlocks ? (a.max_hist_blocks + 31) / 32 : 0;
+  a.bitmap_words = a.max_hist_blocks <= sa::kFuseLimit ? (a.max_hist_blocks + 31) / 32 : 0;
   a.key_fp8 = key_fp8;
+  // candidate lists of the per-token scorer: one per (row, chunk)
+  a.cand_cap = std::min(chunk, sa::kChunkCap);
+  a.cand_row_stride = (size_t)((a.max_hist_blocks + chunk - 1) / chunk) * (size_t)a.cand_cap;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
-  a.cand_count = reinterpret_cast<uint32_t*>(ws + w.count_off);
   a.scores = reinterpret_cast<float*>(ws + w.scores_off);
+  a.cand_meta = reinterpret_cast<uint2*>(ws + w.meta_off);
   a.cand = reinterpret_cast<uint2*>(ws + w.cand_off);
   a.sel_idx = sel_idx;
   if (sa::launch_indexer_topk(a, stream) != hipSuccess) return SA_ERR_HIP;

@@ -10,29 +10,30 @@
 //
 // Pipeline (launches on the caller's stream; a query row is a token, or a
 // (token, KV group) with per-group selection):
-//  1. zero      (histories over kFuseLimit blocks only) clear the per-row
-//               histograms and candidate counters.
-//  2. score     stream every historical index key of a sequence once per pass
+//  1. score     stream every historical index key of a sequence once per pass
 //               and write fp32 scores. Three scorers, by query rows per
 //               sequence: up to 4 rows share a pass of the per-token scorer
 //               (v_dot2 bf16 -> fp32, eight lanes per key, DPP reduction);
 //               16 .. 63 rows take the 16-row MFMA scorer; 64 and more (a
 //               prefill chunk) the MFMA GEMM. One-byte E4M3 keys are widened
-//               to bf16 on the way in. For long histories the per-token scorer
-//               also adds each score to a 2048-bin histogram of the top 11
-//               bits of its order-preserving key.
-//  3. collect   (long histories only) per (row, score chunk): find the
-//               histogram bin that holds the k-th largest score and append
-//               every score at or above that bin to a per-row candidate list.
-//  4. finalize  per row: histogram of the top 11 key bits (built here from
-//               register-held scores for short histories), everything above the
-//               threshold bin is chosen; within the threshold bin the needed
-//               keys are taken by rank (larger key, then lower block id) or, for
-//               large bins, by two more radix levels, the ids tied at the exact
-//               threshold being taken in block order; one scan over the bitmaps
-//               places every chosen id, written ascending. A row whose
-//               threshold bin or candidate list overflows takes an ordered
-//               select over all of its scores instead.
+//               to bf16 on the way in. The per-token scorer also lists, for
+//               each (row, chunk of blocks), its local candidates: every score
+//               at or above the histogram bin that holds the chunk's T-th
+//               largest score, in block order, with that bin's lower edge.
+//  2. select    (per-token scorer) per row: the exact k-th largest key tau_U of
+//               the union of the row's candidate lists; a chunk whose edge lies
+//               above tau_U may hold unlisted keys >= tau_U and is re-read from
+//               its stored scores; the top k of everything >= tau_U (ties at
+//               the k-th key taken in block order) are written ascending.
+//     finalize  (MFMA scorers) per row: histogram of the top 11 key bits from
+//               register-held scores, everything above the threshold bin is
+//               chosen; within the threshold bin the needed keys are taken by
+//               rank (larger key, then lower block id) or, for large bins, by
+//               two more radix levels, the ids tied at the exact threshold
+//               being taken in block order; one scan over the bitmaps places
+//               every chosen id, written ascending.
+//  Rows that do not fit the LDS structures take an ordered select over all of
+//  their stored scores instead.
 
 #include <algorithm>
 
@@ -190,14 +191,6 @@ __device__ void select_bin(const uint32_t* h, int nbins, uint32_t k, uint32_t* s
 }
 
 // ---------------------------------------------------------------------------
-// 1. zero
-// ---------------------------------------------------------------------------
-__global__ void zero_kernel(uint32_t* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
-// ---------------------------------------------------------------------------
 // 2. score
 // ---------------------------------------------------------------------------
 // Sum over the 8 lanes of an aligned lane octet, with DPP moves (no LDS):
@@ -228,7 +221,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 // Score one step for NQ query tokens. Lane q8 of a block's octet holds the
 // 16-byte chunks q8 + 8i of the key: for bf16 keys 8 dims each (i < 4), for fp8
 // keys 16 dims each (i < 2), converted to bf16 pairs before the v_dot2.
-template <int NQ, bool kHist, bool kFp8>
+template <int NQ, bool kFp8>
 __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslot, const int* ncb,
                                            const u32x4* s_q, const u32x4 (&kv)[KeyFmt<kFp8>::kLoads], int beta,
                                            bool in, bool ok, int q8, uint32_t (*s_hist)[kHistBins],
@@ -265,9 +258,8 @@ __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslo
     }
     s = octet_sum(s);
     sc[j] = ok ? s : -INFINITY;   // an unreadable page ranks last
-    if constexpr (kHist) {
-      if (in && q8 == j && beta < ncb[j]) atomicAdd(&s_hist[hslot[j]][score_key(sc[j]) >> 21], 1u);
-    }
+    // the chunk's histogram of the top 11 key bits (lane j of the octet adds row j's score)
+    if (in && q8 == j && beta < ncb[j]) atomicAdd(&s_hist[hslot[j]][score_key(sc[j]) >> 21], 1u);
   }
 }
 
@@ -280,9 +272,10 @@ __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslo
 // other buffers' loads in flight. After a group, lane (octet b, q8 < 4) holds
 // the scores of block 8*q8 + b of the group, so one store per token writes 32
 // consecutive scores (a whole 128-byte line).
-template <int NQ, bool kHist, bool kFp8>
+template <int NQ, bool kFp8>
 __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot, const int* ncb, int lo, int hi,
-                          const int32_t* s_pages, const u32x4* s_q, uint32_t (*s_hist)[kHistBins]) {
+                          const int32_t* s_pages, const u32x4* s_q, uint32_t (*s_hist)[kHistBins],
+                          float (*s_sc)[kCandChunkMax]) {
   constexpr int KB = KeyFmt<kFp8>::kBytes;
   constexpr int KL = KeyFmt<kFp8>::kLoads;
   const int lane = threadIdx.x & 63;
@@ -316,51 +309,124 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
   fill(k3, base + 24 + sub, in3, ok3);
   for (int g = 0; g < ngroups; ++g, base += 32) {
     float keep[NQ], sc[NQ];
-    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k0, base + sub, in0, ok0, q8, s_hist, sc);
+    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k0, base + sub, in0, ok0, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = sc[j];
     fill(k0, base + 32 + sub, in0, ok0);
-    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k1, base + 8 + sub, in1, ok1, q8, s_hist, sc);
+    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k1, base + 8 + sub, in1, ok1, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 1 ? sc[j] : keep[j];
     fill(k1, base + 40 + sub, in1, ok1);
-    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k2, base + 16 + sub, in2, ok2, q8, s_hist, sc);
+    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k2, base + 16 + sub, in2, ok2, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 2 ? sc[j] : keep[j];
     fill(k2, base + 48 + sub, in2, ok2);
-    score_step<NQ, kHist, kFp8>(a, hslot, ncb, s_q, k3, base + 24 + sub, in3, ok3, q8, s_hist, sc);
+    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k3, base + 24 + sub, in3, ok3, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 3 ? sc[j] : keep[j];
     fill(k3, base + 56 + sub, in3, ok3);
     const int beta = base + 8 * q8 + sub;   // the block whose scores this lane keeps (q8 < 4)
     if (q8 < 4 && beta < whi) {
 #pragma unroll
-      for (int j = 0; j < NQ; ++j)
-        if (beta < ncb[j]) a.scores[(size_t)tok[j] * a.max_hist_blocks + beta] = keep[j];
+      for (int j = 0; j < NQ; ++j) {
+        if (beta < ncb[j]) {
+          a.scores[(size_t)tok[j] * a.max_hist_blocks + beta] = keep[j];
+          s_sc[hslot[j]][beta - lo] = keep[j];
+        }
+      }
     }
   }
 }
 
+// Local candidate budget of one chunk of a row: twice the chunk's expected
+// share of the row's top k, plus 4 (at least 8, at most the chunk).
+__device__ __forceinline__ int local_budget(int topk, int chunk_blocks, int row_blocks) {
+  const int share = (2 * topk * chunk_blocks + row_blocks - 1) / max(row_blocks, 1);
+  return min(chunk_blocks, max(8, share + 4));
+}
+
+// Lists the local candidates of one (row, chunk): every key at or above the
+// edge E = the lower end of the 21-bit key prefix (two radix levels of 11 and
+// 10 bits) that holds the chunk's T-th largest key (E = 0 when n <= T: all n),
+// as (key, block id) in ascending block order, and the pair (count, E): every
+// key of the chunk >= E is in the list, which holds about T keys plus those
+// tied with the T-th at 21 bits. A list longer than the capacity is not
+// written; its edge is then 0xFFFFFFFF (no key of the chunk is known to be
+// listed), so the select pass re-reads the chunk. hist (the chunk's level-1
+// histogram) is overwritten.
+__device__ void emit_chunk_candidates(const IndexerArgs& a, int row, int chunk, int nck_all, int lo, int n, int T,
+                                      uint32_t* hist, const float* sc, uint32_t* s_tmp, uint32_t* s_res) {
+  constexpr int kPer = kCandChunkMax / kThreads;
+  // thread i owns entries kPer*i .. kPer*i + kPer - 1 (consecutive blocks)
+  const int e0 = (int)threadIdx.x * kPer;
+  uint32_t keys[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(sc + e0 + i);   // past n: read, never listed
+    keys[i] = score_key(v.x);
+    keys[i + 1] = score_key(v.y);
+    keys[i + 2] = score_key(v.z);
+    keys[i + 3] = score_key(v.w);
+  }
+  uint32_t edge = 0;
+  if (n > T) {
+    select_bin<kThreads>(hist, kHistBins, (uint32_t)T, s_tmp, s_res);
+    const uint32_t b = s_res[0], above = s_res[1];
+    // second level: bits 20..10 of the keys in bin b
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (e0 + i < n && (keys[i] >> 21) == b) atomicAdd(&hist[(keys[i] >> 10) & (kHistBins - 1)], 1u);
+    __syncthreads();
+    select_bin<kThreads>(hist, kHistBins, (uint32_t)T - above, s_tmp, s_res);
+    edge = b << 21 | s_res[0] << 10;
+  }
+  uint32_t take = 0, cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool tk = e0 + i < n && keys[i] >= edge;
+    take |= tk ? 1u << i : 0u;
+    cnt += tk ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t off = block_prefix_exclusive<kThreads>(cnt, s_tmp, &total);
+  const bool overflow = total > (uint32_t)a.cand_cap;
+  if (!overflow) {
+    uint2* dst = a.cand + (size_t)row * a.cand_row_stride + (size_t)chunk * a.cand_cap + off;
+    uint32_t pos = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if ((take >> i) & 1u) dst[pos++] = make_uint2(keys[i], (uint32_t)(lo + e0 + i));
+  }
+  if (threadIdx.x == 0)
+    a.cand_meta[(size_t)row * nck_all + chunk] = overflow ? make_uint2(0u, 0xFFFFFFFFu) : make_uint2(total, edge);
+  __syncthreads();   // the scratch words of the scan and of select_bin are reused by the next row
+}
+
 // Runs of up to GS query tokens of one sequence share a pass over its keys; GS
 // is the host's group size, so a one-token decode does not pay for four query
-// register sets.
-// With kHist the kernel also builds each token's 2048-bin histogram of score
-// keys (needed when the history is too long for finalize to hold all scores).
+// register sets. The workgroup's chunk of every row is kept in LDS (scores and
+// their histogram) and listed as local candidates at the end.
 static_assert(kMaxGroup == 4 && kMaxGroup * (kKeyBytes / 16) <= kThreads, "one index-query load per thread");
+static_assert(kCandChunkMax % (4 * kThreads) == 0, "whole float4 reads of a chunk row");
 
-template <int GS, bool kHist, bool kFp8>
+template <int GS, bool kFp8>
 __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
-  __shared__ uint32_t s_hist[kHist ? GS : 1][kHistBins];
+  __shared__ __align__(16) uint32_t s_hist[GS][kHistBins];
+  __shared__ __align__(16) float s_sc[GS][kCandChunkMax];
   __shared__ int32_t s_pages[kPagePasses * kThreads];   // page ids of the current run's blocks (padded)
   __shared__ u32x4 s_q[kThreads];   // index queries of the current run (padded)
+  __shared__ uint32_t s_tmp[kThreads / 64];
+  __shared__ uint32_t s_res[2];
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const int chunk = blockIdx.x % nchunk;
   const int grp = blockIdx.x / nchunk;
   const int t0 = grp * GS;
   const int ng = min(GS, a.n_tok - t0);
   // Rows are located without the sequence-length check: a row past its
-  // sequence's length is scored all the same (its scores and histogram are
-  // never used), and no read waits for that check.
+  // sequence's length is scored all the same (its lists are never used), and
+  // no read waits for that check.
   int seq[kMaxGroup], ncb[kMaxGroup];
   for (int j = 0; j < kMaxGroup; ++j) {
     ncb[j] = 0;
@@ -373,10 +439,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
   for (int j = 0; j < ng; ++j) any |= ncb[j] > lo;
   if (!any) return;
 
-  if constexpr (kHist) {
-    for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) (&s_hist[0][0])[i] = 0u;
-    __syncthreads();
-  }
+  for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) (&s_hist[0][0])[i] = 0u;
 
   uint32_t done = 0;
   for (int j0 = 0; j0 < ng; ++j0) {
@@ -407,22 +470,23 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
     int pg[kPagePasses];
 #pragma unroll
     for (int r = 0; r < kPagePasses; ++r) pg[r] = prow[min((int)threadIdx.x + r * kThreads, np - 1)];
-    __syncthreads();   // the previous run is done with s_pages and s_q
+    __syncthreads();   // the previous run is done with s_pages and s_q (and the histograms are clear)
     s_q[threadIdx.x] = qv;
 #pragma unroll
     for (int r = 0; r < kPagePasses; ++r) s_pages[threadIdx.x + r * kThreads] = pg[r];
     __syncthreads();
-    if (nq == 1) score_run<1, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist);
-    if constexpr (GS >= 2) { if (nq == 2) score_run<2, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
-    if constexpr (GS >= 3) { if (nq == 3) score_run<3, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
-    if constexpr (GS >= 4) { if (nq == 4) score_run<4, kHist, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist); }
+    if (nq == 1) score_run<1, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc);
+    if constexpr (GS >= 2) { if (nq == 2) score_run<2, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc); }
+    if constexpr (GS >= 3) { if (nq == 3) score_run<3, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc); }
+    if constexpr (GS >= 4) { if (nq == 4) score_run<4, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc); }
   }
-  if constexpr (kHist) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) {
-      const uint32_t v = (&s_hist[0][0])[i];
-      if (v) atomicAdd(&a.hist[(size_t)(t0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
-    }
+  __syncthreads();
+  // each row's local candidates of this chunk
+  for (int j = 0; j < ng; ++j) {
+    if (ncb[j] <= lo) continue;   // (uniform) this chunk holds nothing of row j
+    const int n = min(ncb[j], lo + a.chunk_blocks) - lo;
+    emit_chunk_candidates(a, t0 + j, chunk, nchunk, lo, n, local_budget(a.topk, a.chunk_blocks, ncb[j]), s_hist[j],
+                          s_sc[j], s_tmp, s_res);
   }
 }
 
@@ -732,62 +796,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(IndexerArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. collect
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void collect_kernel(IndexerArgs a) {
-  constexpr int kPer = kCollectChunk / kThreads;
-  __shared__ __align__(16) uint32_t s_h[kHistBins];
-  __shared__ uint32_t s_tmp[4];
-  __shared__ uint32_t s_res[2];
-  __shared__ uint32_t s_base;
-  const int nck = (a.max_hist_blocks + kCollectChunk - 1) / kCollectChunk;
-  const int ck = blockIdx.x % nck;
-  const int t = blockIdx.x / nck;
-  int b, p;
-  const int ncand = min(located_blocks(a, t, &b, &p), a.max_hist_blocks);
-  const int len = seq_len_of(a, b);   // consumed once the loads below are in flight
-  const int lo = ck * kCollectChunk;
-  if (ncand <= kFuseLimit || lo >= ncand) return;   // short histories select in finalize
-  const int hi = min(ncand, lo + kCollectChunk);
-  // issue every load first: this chunk's scores (coalesced) and the histogram
-  const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
-  float sv[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int beta = lo + j * kThreads + (int)threadIdx.x;
-    sv[j] = beta < hi ? srow[beta] : 0.f;
-  }
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_h[i] = a.hist[(size_t)t * kHistBins + i];
-  __syncthreads();
-  select_bin<kThreads>(s_h, kHistBins, (uint32_t)a.topk, s_tmp, s_res);
-  const uint32_t b1 = s_res[0];
-  uint32_t takes = 0, cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int beta = lo + j * kThreads + (int)threadIdx.x;
-    const bool take = beta < hi && (score_key(sv[j]) >> 21) >= b1;
-    takes |= take ? (1u << j) : 0u;
-    cnt += take ? 1u : 0u;
-  }
-  uint32_t total;
-  const uint32_t off = block_prefix_exclusive<kThreads>(cnt, s_tmp, &total);
-  if (total == 0 || !token_valid(a, b, p, len)) return;   // an invalid token lists nothing
-  if (threadIdx.x == 0) s_base = atomicAdd(&a.cand_count[t], total);
-  __syncthreads();
-  uint32_t pos = s_base + off;
-  uint2* crow = a.cand + (size_t)t * kCandCap;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if ((takes >> j) & 1u) {
-      if (pos < (uint32_t)kCandCap)
-        crow[pos] = make_uint2(score_key(sv[j]), (uint32_t)(lo + j * kThreads + (int)threadIdx.x));
-      ++pos;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 4. finalize
+// 3. finalize (MFMA scorers) and the ordered select shared by both selects
 // ---------------------------------------------------------------------------
 constexpr int kFinalThreads = 512;
 
@@ -806,7 +815,7 @@ __device__ __forceinline__ uint32_t tz_block(uint64_t e) { return ~(uint32_t)e; 
 // (chosen, tied) counts gives its offsets (one barrier), and it places its ids
 // -- taking the leading tied ids of its range -- in LDS (s_ids, k entries),
 // which is then written out in one coalesced pass.
-constexpr int kEmitWords = kBitmapMaxBlocks / 32 / kFinalThreads + 1;
+constexpr int kEmitWords = kFuseLimit / 32 / kFinalThreads + 1;
 
 __device__ __forceinline__ void emit_selection(const uint32_t* sel_bm, const uint32_t* eq_bm, uint32_t need_eq, int nbits, int k,
                                int32_t* out, uint32_t* s_tmp, int32_t* s_ids) {
@@ -888,97 +897,94 @@ struct alignas(16) FinalizeLds {
   uint32_t n_tz;
 };
 
-// Exact k-th largest key over all of a token's scores (three radix levels, the
-// first from the score pass's histogram); *count_gt receives how many keys are
-// strictly larger.
-__device__ uint32_t radix_kth_global(const IndexerArgs& a, FinalizeLds& s, int t, int ncand, uint32_t k,
-                                     uint32_t* count_gt) {
-  const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+// Exact k-th largest (k >= 1, at most m) of the keys key_at(0 .. m-1): three
+// radix levels of 11, 11 and 10 bits, histograms in h[kHistBins]; *count_gt
+// receives how many keys are strictly larger. NT threads, all of them call it.
+template <int NT, typename KeyAt>
+__device__ uint32_t radix_kth(KeyAt key_at, int m, uint32_t k, uint32_t* h, uint32_t* tmp, uint32_t* res,
+                              uint32_t* count_gt) {
   __syncthreads();
-  if (ncand <= kFuseLimit) {   // no histogram from the score pass: build the first level here
-    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < ncand; i += kFinalThreads) atomicAdd(&s.h[score_key(srow[i]) >> 21], 1u);
-  } else {
-    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
-  }
-  __syncthreads();
-  select_bin<kFinalThreads>(s.h, kHistBins, k, s.tmp, s.res);
-  uint32_t prefix = s.res[0] << 21;
-  uint32_t above = s.res[1];
-  __syncthreads();
-  const int shifts[2] = {10, 0};
-  const int widths[2] = {11, 10};
-  for (int lvl = 0; lvl < 2; ++lvl) {
+  uint32_t prefix = 0, above = 0;
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int lvl = 0; lvl < 3; ++lvl) {
     const int sh = shifts[lvl];
     const int nb = 1 << widths[lvl];
     const int hs = sh + widths[lvl];
-    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
+    for (int i = threadIdx.x; i < kHistBins; i += NT) h[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < ncand; i += kFinalThreads) {
-      const uint32_t key = score_key(srow[i]);
-      if ((key >> hs) == (prefix >> hs)) atomicAdd(&s.h[(key >> sh) & (uint32_t)(nb - 1)], 1u);
+    for (int i = threadIdx.x; i < m; i += NT) {
+      const uint32_t key = key_at(i);
+      if (lvl == 0 || (key >> hs) == (prefix >> hs)) atomicAdd(&h[(key >> sh) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    select_bin<kFinalThreads>(s.h, nb, k - above, s.tmp, s.res);
-    prefix |= s.res[0] << sh;
-    above += s.res[1];
+    select_bin<NT>(h, nb, k - above, tmp, res);
+    prefix |= res[0] << sh;
+    above += res[1];
     __syncthreads();
   }
   *count_gt = above;
   return prefix;
 }
 
-// Selection over all scores in one ordered pass (used when the threshold bin
-// or the candidate list overflows, or the history is too long for the LDS
-// bitmaps): keys above tau, then keys equal to tau in block order until k are
-// taken; the output comes out ascending.
-__device__ void select_ordered_global(const IndexerArgs& a, FinalizeLds& s, int t, int ncand, int32_t* out) {
+// The same over all of a token's stored scores.
+template <int NT>
+__device__ uint32_t radix_kth_global(const IndexerArgs& a, uint32_t* h, uint32_t* tmp, uint32_t* res, int t,
+                                     int ncand, uint32_t k, uint32_t* count_gt) {
+  const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+  return radix_kth<NT>([srow](int i) { return score_key(srow[i]); }, ncand, k, h, tmp, res, count_gt);
+}
+
+// Selection over all scores in one ordered pass (used when a row does not fit
+// the LDS structures of either select): keys above tau, then keys equal to tau
+// in block order until k are taken; the output comes out ascending.
+template <int NT>
+__device__ void select_ordered_global(const IndexerArgs& a, uint32_t* h, uint32_t* tmp, uint32_t* res, int t,
+                                      int ncand, int32_t* out) {
   const int k = a.topk;
   uint32_t count_gt;
-  const uint32_t tau = radix_kth_global(a, s, t, ncand, (uint32_t)k, &count_gt);
+  const uint32_t tau = radix_kth_global<NT>(a, h, tmp, res, t, ncand, (uint32_t)k, &count_gt);
   count_gt = min(count_gt, (uint32_t)k);
   const uint32_t need_eq = (uint32_t)k - count_gt;
   const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
   uint32_t eq_before = 0, sel_before = 0;
-  for (int base = 0; base < ncand; base += kFinalThreads) {
+  for (int base = 0; base < ncand; base += NT) {
     const int beta = base + threadIdx.x;
     uint32_t key = 0;
     if (beta < ncand) key = score_key(srow[beta]);
     const bool gt = beta < ncand && key > tau;
     const bool eq = beta < ncand && key == tau;
     uint32_t eq_tot, sel_tot;
-    const uint32_t eq_rank = eq_before + block_prefix_exclusive<kFinalThreads>(eq ? 1u : 0u, s.tmp, &eq_tot);
+    const uint32_t eq_rank = eq_before + block_prefix_exclusive<NT>(eq ? 1u : 0u, tmp, &eq_tot);
     const bool take = gt || (eq && eq_rank < need_eq);
-    const uint32_t pos = sel_before + block_prefix_exclusive<kFinalThreads>(take ? 1u : 0u, s.tmp, &sel_tot);
+    const uint32_t pos = sel_before + block_prefix_exclusive<NT>(take ? 1u : 0u, tmp, &sel_tot);
     if (take && pos < (uint32_t)k) out[pos] = beta;
     eq_before += eq_tot;
     sel_before += sel_tot;
   }
 }
 
-// Histogram and classification of one token's scores. KP > 0: a history of
-// at most KP * kFinalThreads blocks whose scores are held in registers, KP per
-// thread (instantiated for 2 .. 32 so that short histories execute no steps
-// past their own); KP == 0: a longer history, from the score pass's histogram
-// and the collect pass's candidates. Afterwards sel_bm holds the ids above the
-// threshold bin b1 (*above of them) and s.tz the threshold-bin entries.
-// Returns kClassified, kDone (an invalid token: its output is written) or
-// kFallback (the history does not fit the LDS structures: the caller selects
-// it in order over all scores).
+// Histogram and classification of one token's scores: a history of at most
+// KP * kFinalThreads blocks whose scores are held in registers, KP per thread
+// (instantiated for 2 .. 32 so that short histories execute no steps past
+// their own). Afterwards sel_bm holds the ids above the threshold bin b1
+// (*above of them) and s.tz the threshold-bin entries. Returns kClassified,
+// kDone (an invalid token: its output is written) or kFallback (the threshold
+// bin does not fit the LDS structures: the caller selects the row in order
+// over all scores).
 enum ClassifyResult { kClassified, kDone, kFallback };
 
 template <int KP>
 __device__ __forceinline__ ClassifyResult finalize_classify(const IndexerArgs& a, FinalizeLds& s, uint32_t* sel_bm, uint32_t* eq_bm, int t,
                                   int ncand, bool valid, int32_t* out, uint32_t* b1_out, uint32_t* above_out) {
-  constexpr bool kFused = KP > 0;
-  constexpr int kPer = kFused ? KP : 1;
+  static_assert(KP > 0, "scores held in registers");
+  constexpr int kPer = KP;
   constexpr int kGroup = kPer < 8 ? kPer : 8;   // steps whose loads are issued together
   const int k = a.topk;
   const int nw = (ncand + 31) >> 5;   // bitmap words this token needs
   const int jmax = (ncand + kFinalThreads - 1) / kFinalThreads;   // steps j that hold scores (uniform)
   uint32_t kv[kPer];
-  if constexpr (kFused) {
+  {
     // every load of a group is issued (past the history they re-read its last
     // score), so all of them are in flight at once
     const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
@@ -994,8 +1000,6 @@ __device__ __forceinline__ ClassifyResult finalize_classify(const IndexerArgs& a
     for (int j = 0; j < kPer; ++j)
       kv[j] = j < jmax && j * kFinalThreads + (int)threadIdx.x < ncand ? score_key(sv[j]) : 0u;
     for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = 0u;
-  } else {
-    for (int i = threadIdx.x; i < kHistBins; i += kFinalThreads) s.h[i] = a.hist[(size_t)t * kHistBins + i];
   }
   if (nw <= a.bitmap_words) {
     for (int i = threadIdx.x; i < nw; i += kFinalThreads) {
@@ -1005,16 +1009,14 @@ __device__ __forceinline__ ClassifyResult finalize_classify(const IndexerArgs& a
   }
   if (threadIdx.x == 0) s.n_tz = 0;
   __syncthreads();
-  if constexpr (kFused) {   // the score pass built no histogram for short histories
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (j < jmax) {
-        const int beta = j * kFinalThreads + (int)threadIdx.x;
-        if (beta < ncand) atomicAdd(&s.h[kv[j] >> 21], 1u);
-      }
+  for (int j = 0; j < kPer; ++j) {
+    if (j < jmax) {
+      const int beta = j * kFinalThreads + (int)threadIdx.x;
+      if (beta < ncand) atomicAdd(&s.h[kv[j] >> 21], 1u);
     }
-    __syncthreads();
   }
+  __syncthreads();
   if (!valid) {   // past its sequence's length: selects nothing
     for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = -1;
     return kDone;
@@ -1023,63 +1025,48 @@ __device__ __forceinline__ ClassifyResult finalize_classify(const IndexerArgs& a
   const uint32_t b1 = s.res[0];
   const uint32_t above = min(s.res[1], (uint32_t)k - 1u);
   const uint32_t in_bin = s.h[b1];
-  const uint32_t n_listed = kFused ? 0u : a.cand_count[t];
-  if (nw > a.bitmap_words || in_bin > (uint32_t)kTieCap || (!kFused && n_listed > (uint32_t)kCandCap))
-    return kFallback;
+  if (nw > a.bitmap_words || in_bin > (uint32_t)kTieCap) return kFallback;
   *b1_out = b1;
   *above_out = above;
-  if constexpr (kFused) {
-    // A wave holds 64 consecutive block ids per j: its ballot of "above the
-    // threshold bin" is exactly two bitmap words, and the threshold-bin keys
-    // take one counter update per wave.
-    // Lane j keeps the two words of step j; they are stored once at the end.
-    const int lane = threadIdx.x & 63;
-    uint32_t n_wave = 0;   // this wave's threshold-bin keys (first pass: count)
-    uint32_t word_lo = 0, word_hi = 0;
+  // A wave holds 64 consecutive block ids per j: its ballot of "above the
+  // threshold bin" is exactly two bitmap words, and the threshold-bin keys
+  // take one counter update per wave.
+  // Lane j keeps the two words of step j; they are stored once at the end.
+  const int lane = threadIdx.x & 63;
+  uint32_t n_wave = 0;   // this wave's threshold-bin keys (first pass: count)
+  uint32_t word_lo = 0, word_hi = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (j < jmax) {
+      const bool in = j * kFinalThreads + (int)threadIdx.x < ncand;
+      const uint32_t bin = kv[j] >> 21;
+      const uint64_t above_mask = __ballot(in && bin > b1);
+      word_lo = lane == j ? (uint32_t)above_mask : word_lo;
+      word_hi = lane == j ? (uint32_t)(above_mask >> 32) : word_hi;
+      n_wave += (uint32_t)__popcll(__ballot(in && bin == b1));
+    }
+  }
+  if (lane < jmax) {
+    const int w = (lane * kFinalThreads + (int)(threadIdx.x - lane)) >> 5;
+    if (w < nw) sel_bm[w] = word_lo;
+    if (w + 1 < nw) sel_bm[w + 1] = word_hi;
+  }
+  if (n_wave != 0u) {   // second pass: slots base + rank within the wave
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&s.n_tz, n_wave);
+    base = __shfl(base, 0);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       if (j < jmax) {
-        const bool in = j * kFinalThreads + (int)threadIdx.x < ncand;
-        const uint32_t bin = kv[j] >> 21;
-        const uint64_t above_mask = __ballot(in && bin > b1);
-        word_lo = lane == j ? (uint32_t)above_mask : word_lo;
-        word_hi = lane == j ? (uint32_t)(above_mask >> 32) : word_hi;
-        n_wave += (uint32_t)__popcll(__ballot(in && bin == b1));
-      }
-    }
-    if (lane < jmax) {
-      const int w = (lane * kFinalThreads + (int)(threadIdx.x - lane)) >> 5;
-      if (w < nw) sel_bm[w] = word_lo;
-      if (w + 1 < nw) sel_bm[w + 1] = word_hi;
-    }
-    if (n_wave != 0u) {   // second pass: slots base + rank within the wave
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&s.n_tz, n_wave);
-      base = __shfl(base, 0);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (j < jmax) {
-          const int beta = j * kFinalThreads + (int)threadIdx.x;
-          const bool tz = beta < ncand && (kv[j] >> 21) == b1;
-          const uint64_t tz_mask = __ballot(tz);
-          const uint32_t slot = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(tz_mask >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)tz_mask, 0u));
-          if (tz && slot < (uint32_t)kTieCap) {
-            s.tz[slot] = tz_entry(kv[j], (uint32_t)beta);
-          }
-          base += (uint32_t)__popcll(tz_mask);
+        const int beta = j * kFinalThreads + (int)threadIdx.x;
+        const bool tz = beta < ncand && (kv[j] >> 21) == b1;
+        const uint64_t tz_mask = __ballot(tz);
+        const uint32_t slot = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(tz_mask >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)tz_mask, 0u));
+        if (tz && slot < (uint32_t)kTieCap) {
+          s.tz[slot] = tz_entry(kv[j], (uint32_t)beta);
         }
-      }
-    }
-  } else {
-    for (uint32_t i = threadIdx.x; i < n_listed; i += kFinalThreads) {
-      const uint2 c = a.cand[(size_t)t * kCandCap + i];
-      const uint32_t key = c.x, beta = c.y, bin = key >> 21;
-      if (bin > b1) {
-        atomicOr(&sel_bm[beta >> 5], 1u << (beta & 31));
-      } else if (bin == b1) {
-        const uint32_t slot = atomicAdd(&s.n_tz, 1u);
-        if (slot < (uint32_t)kTieCap) s.tz[slot] = tz_entry(key, beta);
+        base += (uint32_t)__popcll(tz_mask);
       }
     }
   }
@@ -1092,8 +1079,8 @@ __device__ __forceinline__ ClassifyResult finalize_classify(const IndexerArgs& a
 // bin. Ranking the threshold bin's entries, or two more radix levels over their
 // keys, completes the selection: keys above the exact k-th key tau are chosen,
 // and keys equal to tau in block order until k are taken. emit_selection writes
-// the chosen ids ascending. Short histories read their scores directly, long
-// ones the candidates gathered by collect_kernel.
+// the chosen ids ascending. Used after the MFMA scorers (histories of at most
+// kFuseLimit blocks).
 __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) {
   __shared__ FinalizeLds s;
   extern __shared__ uint32_t s_bm[];   // [2][bitmap_words]: chosen ids, ids tied at tau
@@ -1116,14 +1103,14 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   const int jmax = (ncand + kFinalThreads - 1) / kFinalThreads;
   uint32_t b1 = 0, above = 0;
   ClassifyResult r;
-  if (ncand > kFuseLimit) r = finalize_classify<0>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
+  if (ncand > kFuseLimit) r = kFallback;   // (the host never sends such a row here)
   else if (jmax <= 2) r = finalize_classify<2>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
   else if (jmax <= 4) r = finalize_classify<4>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
   else if (jmax <= 8) r = finalize_classify<8>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
   else if (jmax <= 16) r = finalize_classify<16>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
   else r = finalize_classify<32>(a, s, sel_bm, eq_bm, t, ncand, valid, out, &b1, &above);
   static_assert(kFuseLimit == 32 * kFinalThreads, "the largest instantiation covers every fused history");
-  if (r == kFallback) select_ordered_global(a, s, t, ncand, out);
+  if (r == kFallback) select_ordered_global<kFinalThreads>(a, s.h, s.tmp, s.res, t, ncand, out);
   if (r != kClassified) return;
   const int m = (int)min(s.n_tz, (uint32_t)kTieCap);
   const uint32_t need = (uint32_t)k - above;
@@ -1181,31 +1168,244 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   emit_selection(sel_bm, eq_bm, need_eq, ncand, k, out, s.tmp, reinterpret_cast<int32_t*>(s.tz));
 }
 
+// ---------------------------------------------------------------------------
+// 4. select (after the per-token scorer)
+// ---------------------------------------------------------------------------
+// One workgroup per row. The row's candidate lists are read in chunk order, so
+// the union U is in ascending block order. tau_U = the k-th largest key of U is
+// a lower bound of the row's k-th largest key tau. A chunk whose edge is at or
+// below tau_U listed every key >= tau_U it holds; a chunk whose edge lies above
+// tau_U (a list that stopped above tau_U, or one that did not fit) is re-read
+// from its stored scores. Then F = every key >= tau_U of the row, in block
+// order, holds the top k: the keys above tau are chosen and the keys equal to
+// tau in block order until k are taken, and the chosen ids come out ascending.
+// A row whose lists or F do not fit in LDS takes the ordered select over all
+// of its stored scores.
+constexpr int kSelThreads = 512;
+constexpr int kSelCap = 6144;                     // list entries of one row held in LDS
+constexpr int kSelMaxChunks = 1024;               // chunks of one row
+constexpr int kSelPer = kSelCap / kSelThreads;    // entries per thread in the ordered pass
+constexpr int kSelChunksPer = kSelMaxChunks / kSelThreads;
+
+struct alignas(16) SelectLds {
+  uint32_t key[kSelCap];    // U: the row's lists in chunk (= block) order
+  uint32_t id[kSelCap];
+  uint32_t fkey[kSelCap];   // F, when some chunk had to be re-read
+  uint32_t fid[kSelCap];
+  uint32_t h[kHistBins];
+  uint32_t off[kSelMaxChunks + 1];    // first entry of each chunk's list in U
+  uint32_t foff[kSelMaxChunks + 1];   // first entry of each chunk in F (its count, before the scan)
+  uint32_t edge[kSelMaxChunks];
+  uint32_t tmp[2 * (kSelThreads / 64)];
+  uint32_t res[2];
+};
+
+// Exclusive scan of v[0 .. n) in place (n <= kSelMaxChunks); v[n] = total.
+__device__ void chunk_scan(uint32_t* v, int n, uint32_t* tmp) {
+  uint32_t c[kSelChunksPer];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int r = 0; r < kSelChunksPer; ++r) {
+    const int i = (int)threadIdx.x * kSelChunksPer + r;
+    c[r] = i < n ? v[i] : 0u;
+    sum += c[r];
+  }
+  uint32_t total;
+  uint32_t ex = block_prefix_exclusive<kSelThreads>(sum, tmp, &total);
+#pragma unroll
+  for (int r = 0; r < kSelChunksPer; ++r) {
+    const int i = (int)threadIdx.x * kSelChunksPer + r;
+    if (i < n) v[i] = ex;
+    ex += c[r];
+  }
+  if (threadIdx.x == 0) v[n] = total;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
+  constexpr int kWaves = kSelThreads / 64;
+  __shared__ SelectLds s;
+  const int t = blockIdx.x;
+  const int k = a.topk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int b, p;
+  const int ncand = min(located_blocks(a, t, &b, &p), a.max_hist_blocks);
+  const int len = seq_len_of(a, b);
+  int32_t* out = a.sel_idx + (size_t)t * k;
+  const bool valid = token_valid(a, b, p, len);
+  if (!valid || ncand <= k) {   // nothing, or every historical block
+    const int nv = valid ? ncand : 0;
+    for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
+  const int C = a.chunk_blocks;
+  const int nck_all = (a.max_hist_blocks + C - 1) / C;
+  const int nck = (ncand + C - 1) / C;
+  if (nck > kSelMaxChunks) {
+    select_ordered_global<kSelThreads>(a, s.h, s.tmp, s.res, t, ncand, out);
+    return;
+  }
+  const uint2* meta = a.cand_meta + (size_t)t * nck_all;
+  const uint2* lists = a.cand + (size_t)t * a.cand_row_stride;
+  const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
+
+  // 1. list lengths and edges; first entry of every list in U
+  for (int c = threadIdx.x; c < nck; c += kSelThreads) {
+    const uint2 m = meta[c];
+    s.off[c] = m.x;
+    s.edge[c] = m.y;
+  }
+  __syncthreads();
+  chunk_scan(s.off, nck, s.tmp);
+  const uint32_t m_u = s.off[nck];
+  if (m_u > (uint32_t)kSelCap) {
+    select_ordered_global<kSelThreads>(a, s.h, s.tmp, s.res, t, ncand, out);
+    return;
+  }
+  // 2. U in chunk order (a wave per list)
+  for (int c = wave; c < nck; c += kWaves) {
+    const uint32_t o = s.off[c], n = s.off[c + 1] - o;
+    const uint2* src = lists + (size_t)c * a.cand_cap;
+    for (uint32_t j = lane; j < n; j += 64) {
+      const uint2 e = src[j];
+      s.key[o + j] = e.x;
+      s.id[o + j] = e.y;
+    }
+  }
+  __syncthreads();
+  // 3. tau_U (every key, 0, when fewer than k are listed)
+  uint32_t gt = 0;
+  uint32_t tau = 0;
+  if (m_u >= (uint32_t)k) {
+    const uint32_t* keys = s.key;
+    tau = radix_kth<kSelThreads>([keys](int i) { return keys[i]; }, (int)m_u, (uint32_t)k, s.h, s.tmp, s.res, &gt);
+  }
+  // 4. chunks that may hold unlisted keys >= tau_U
+  bool mine = m_u < (uint32_t)k;
+  for (int c = threadIdx.x; c < nck; c += kSelThreads) mine |= s.edge[c] > tau;
+  const bool reread = __syncthreads_or(mine);
+  const uint32_t* fkey = s.key;
+  const uint32_t* fid = s.id;
+  uint32_t mf = m_u;
+  if (reread) {
+    const uint32_t tau_u = tau;
+    // F's count per chunk: its listed keys >= tau_U, or its stored keys >= tau_U
+    for (int c = wave; c < nck; c += kWaves) {
+      uint32_t n_f = 0;
+      if (s.edge[c] > tau_u) {
+        const int lo = c * C, hi = min(ncand, lo + C);
+        for (int j = lo + lane; j - lane < hi; j += 64)
+          n_f += (uint32_t)__popcll(__ballot(j < hi && score_key(srow[min(j, hi - 1)]) >= tau_u));
+      } else {
+        const uint32_t o = s.off[c], o1 = s.off[c + 1];
+        for (uint32_t j = o + lane; j - lane < o1; j += 64)
+          n_f += (uint32_t)__popcll(__ballot(j < o1 && s.key[min(j, o1 - 1)] >= tau_u));
+      }
+      if (lane == 0) s.foff[c] = n_f;
+    }
+    __syncthreads();
+    chunk_scan(s.foff, nck, s.tmp);
+    mf = s.foff[nck];
+    if (mf > (uint32_t)kSelCap) {
+      select_ordered_global<kSelThreads>(a, s.h, s.tmp, s.res, t, ncand, out);
+      return;
+    }
+    // F in block order
+    for (int c = wave; c < nck; c += kWaves) {
+      uint32_t pos = s.foff[c];
+      if (s.edge[c] > tau_u) {
+        const int lo = c * C, hi = min(ncand, lo + C);
+        for (int j = lo + lane; j - lane < hi; j += 64) {
+          const uint32_t key = score_key(srow[min(j, hi - 1)]);
+          const bool in = j < hi && key >= tau_u;
+          const uint64_t mask = __ballot(in);
+          const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          if (in) {
+            s.fkey[pos + r] = key;
+            s.fid[pos + r] = (uint32_t)j;
+          }
+          pos += (uint32_t)__popcll(mask);
+        }
+      } else {
+        const uint32_t o = s.off[c], o1 = s.off[c + 1];
+        for (uint32_t j = o + lane; j - lane < o1; j += 64) {
+          const uint32_t jj = min(j, o1 - 1);
+          const uint32_t key = s.key[jj];
+          const bool in = j < o1 && key >= tau_u;
+          const uint64_t mask = __ballot(in);
+          const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          if (in) {
+            s.fkey[pos + r] = key;
+            s.fid[pos + r] = s.id[jj];
+          }
+          pos += (uint32_t)__popcll(mask);
+        }
+      }
+    }
+    __syncthreads();
+    fkey = s.fkey;
+    fid = s.fid;
+    tau = radix_kth<kSelThreads>([fkey](int i) { return fkey[i]; }, (int)mf, (uint32_t)k, s.h, s.tmp, s.res, &gt);
+  }
+  // 5. keys above tau, then keys equal to tau in block order until k are
+  // taken; thread i owns entries kSelPer*i .. +kSelPer of F (or of U)
+  const uint32_t need_eq = (uint32_t)k - min(gt, (uint32_t)k);
+  const int i0 = (int)threadIdx.x * kSelPer;
+  uint32_t kk[kSelPer];
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    kk[i] = i0 + i < (int)mf ? fkey[i0 + i] : 0u;
+    n_eq += (i0 + i < (int)mf && kk[i] == tau) ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t eq_seen = block_prefix_exclusive<kSelThreads>(n_eq, s.tmp, &tot);
+  uint32_t takes = 0, n_take = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const bool in = i0 + i < (int)mf;
+    const bool eq = in && kk[i] == tau;
+    const bool take = (in && kk[i] > tau) || (eq && eq_seen < need_eq);
+    eq_seen += eq ? 1u : 0u;
+    takes |= take ? 1u << i : 0u;
+    n_take += take ? 1u : 0u;
+  }
+  uint32_t pos = block_prefix_exclusive<kSelThreads>(n_take, s.tmp, &tot);
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    if ((takes >> i) & 1u) {
+      if (pos < (uint32_t)k) out[pos] = (int32_t)fid[i0 + i];
+      ++pos;
+    }
+  }
+  for (int i = (int)min(tot, (uint32_t)k) + (int)threadIdx.x; i < k; i += kSelThreads) out[i] = -1;   // (never: tot = k)
+}
+
 }  // namespace
+
+size_t indexer_cand_row_bound(int max_hist_blocks) {
+  size_t most = 0;
+  for (int c = 64; c <= kCandChunkMax; c <<= 1) {
+    const size_t chunks = (size_t)((max_hist_blocks + c - 1) / c);
+    most = std::max(most, chunks * (size_t)std::min(c, kChunkCap));
+  }
+  return most;
+}
 
 IndexerWorkspace indexer_workspace_layout(int n_tok, int max_pages_per_seq) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   IndexerWorkspace w;
   const size_t nt = (size_t)(n_tok > 0 ? n_tok : 0);
-  const size_t mhb = (size_t)(max_pages_per_seq > 0 ? max_pages_per_seq : 0) * kBlocksPerPage;
-  w.hist_off = 0;
-  w.count_off = up(nt * kHistBins * 4);
-  w.scores_off = w.count_off + up(nt * 4);
-  w.cand_off = w.scores_off + up(nt * mhb * 4);
-  w.total = w.cand_off + up(nt * kCandCap * 8);
+  const int mhb = (max_pages_per_seq > 0 ? max_pages_per_seq : 0) * kBlocksPerPage;
+  w.scores_off = 0;
+  w.meta_off = up(nt * (size_t)mhb * 4);
+  w.cand_off = w.meta_off + up(nt * (size_t)((mhb + 63) / 64) * 8);   // chunks are at least 64 blocks
+  w.total = w.cand_off + up(nt * indexer_cand_row_bound(mhb) * 8);
   return w;
 }
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
   if (a.n_tok == 0) return hipSuccess;
-  // Histories longer than kFuseLimit need the score pass's histograms and the
-  // collect pass; shorter ones are selected by finalize alone.
-  const bool long_hist = a.max_hist_blocks > kFuseLimit;
-  if (long_hist) {   // histograms and candidate counters sit next to each other in the workspace
-    const size_t nzero = (reinterpret_cast<const uint8_t*>(a.scores) - reinterpret_cast<const uint8_t*>(a.hist)) / 4;
-    const unsigned zblocks = (unsigned)std::min<size_t>((nzero + 1023) / 1024, 2048);
-    zero_kernel<<<zblocks, 1024, 0, stream>>>(a.hist, nzero);
-  }
   if (a.use_gemm) {
     const int ntt = (a.n_tok + kGemmTokens - 1) / kGemmTokens;
     const int ntiles = (a.max_hist_blocks + kGemmBlocks - 1) / kGemmBlocks;
@@ -1221,7 +1421,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
     finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
     return hipGetLastError();
   }
-  if (a.use_mfma16) {   // never with long histories (the host checks)
+  if (a.use_mfma16) {   // never with histories over kFuseLimit (the host checks)
     const int nrg = (a.n_tok + kMfmaRows - 1) / kMfmaRows;
     const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
     const dim3 grid((unsigned)((long long)nrg * nchunk));
@@ -1233,15 +1433,10 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
   const int ngroups = (a.n_tok + a.group_size - 1) / a.group_size;
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const dim3 sgrid((unsigned)((long long)ngroups * nchunk));
-#define SA_SCORE(GS)                                                                     \
-  do {                                                                                   \
-    if (a.key_fp8) {                                                                     \
-      if (long_hist) score_kernel<GS, true, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);   \
-      else score_kernel<GS, false, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);            \
-    } else {                                                                             \
-      if (long_hist) score_kernel<GS, true, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);  \
-      else score_kernel<GS, false, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);           \
-    }                                                                                    \
+#define SA_SCORE(GS)                                                                            \
+  do {                                                                                          \
+    if (a.key_fp8) score_kernel<GS, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);             \
+    else score_kernel<GS, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);                      \
   } while (0)
   switch (a.group_size) {
     case 1: SA_SCORE(1); break;
@@ -1250,11 +1445,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
     default: SA_SCORE(4); break;
   }
 #undef SA_SCORE
-  if (long_hist) {
-    const int nck = (a.max_hist_blocks + kCollectChunk - 1) / kCollectChunk;
-    collect_kernel<<<dim3((unsigned)((long long)a.n_tok * nck)), dim3(kThreads), 0, stream>>>(a);
-  }
-  finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
+  select_kernel<<<dim3((unsigned)a.n_tok), dim3(kSelThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -22,10 +22,9 @@ constexpr int kKeyBytes = kIdxDim * 2;                     // one index key
 
 // indexer workspace
 constexpr int kHistBins = 2048;       // first radix digit: key bits 31..21
-constexpr int kCandCap = 4096;        // candidates kept per token for the in-LDS finish
-constexpr int kCollectChunk = 4096;   // scores per collect workgroup
-constexpr int kFuseLimit = 16384;          // histories up to this many blocks are selected by finalize alone
-constexpr int kBitmapMaxBlocks = 1 << 17;   // longest history the finalize bitmaps cover (2 x 16 KB LDS)
+constexpr int kFuseLimit = 16384;     // longest history the MFMA scorers' finalize holds in registers
+constexpr int kCandChunkMax = 2048;   // longest block chunk of one per-token score workgroup
+constexpr int kChunkCap = 512;        // candidates one (row, chunk) may list
 
 struct AttnArgs {
   const uint8_t* q;
@@ -71,20 +70,26 @@ struct IndexerArgs {
   int max_hist_blocks;      // max_pages * 8: stride of the score rows
   int group_size;           // query tokens scored per pass over a sequence's keys
   int chunk_blocks;         // blocks per score workgroup
-  int bitmap_words;         // LDS bitmap words per finalize workgroup (0: ordered select over all scores)
+  int bitmap_words;         // LDS bitmap words per finalize workgroup (MFMA scorers)
   bool use_gemm;            // score with the MFMA GEMM kernel (long runs of tokens per sequence)
   bool use_mfma16;          // score 16 query rows per pass with MFMA (16 .. 63 rows per sequence)
   bool key_fp8;             // index keys are one-byte OCP E4M3 codes (else bf16)
   int32_t* sel_idx;
-  uint32_t* hist;           // [n_tok][kHistBins]
-  uint32_t* cand_count;     // [n_tok]
   float* scores;            // [n_tok][max_hist_blocks]
-  uint2* cand;              // [n_tok][kCandCap] (key, block)
+  // per-token scorer: each (row, chunk) lists its local candidates
+  int cand_cap;             // list capacity per (row, chunk): min(chunk_blocks, kChunkCap)
+  size_t cand_row_stride;   // list entries per row: chunks x cand_cap
+  uint2* cand;              // [n_tok][chunks][cand_cap] (key, block), ascending block ids
+  uint2* cand_meta;         // [n_tok][chunks] (count, edge key: every key >= edge is listed)
 };
 
 struct IndexerWorkspace {
-  size_t hist_off, count_off, scores_off, cand_off, total;
+  size_t scores_off, meta_off, cand_off, total;
 };
+
+// Candidate-list entries per row the workspace holds for a history of
+// max_hist_blocks blocks, over every chunk length the host may pick.
+size_t indexer_cand_row_bound(int max_hist_blocks);
 
 IndexerWorkspace indexer_workspace_layout(int n_tok, int max_pages_per_seq);
 

@@ -54,8 +54,15 @@ def test_workspace_size(lib):
     c = lib.sa_indexer_topk_workspace_size(2, 256, 512)
     assert 0 < a < b < c
     assert a % 256 == 0
-    # scores (4 B per historical block) + 2048-bin histogram + candidates per token
-    assert a >= 128 * 8 * 4 + 2048 * 4 + 4096 * 8
+    # per token: scores (4 B per historical block), one (count, edge) pair per
+    # chunk of at least 64 blocks, and candidate lists (8 B per entry) for every
+    # chunk length the host may pick: up to 512 entries per chunk, at most the chunk
+    blocks = 128 * 8
+    lists = max(-(-blocks // c) * min(c, 512) for c in (64, 128, 256, 512, 1024, 2048))
+    assert lists == blocks
+    assert a >= blocks * 4 + (blocks // 64) * 8 + lists * 8
+    # the 128K verify batch fits the no-alloc entry point's scratch array
+    assert lib.sa_indexer_topk_workspace_size(256, 2048, 512) <= 64 << 20
 
 
 def test_resolve_num_splits(lib):
@@ -131,7 +138,8 @@ def test_sparse_decode_validation(lib):
     assert call(topk=0) == ops.SA_ERR_UNSUPPORTED
     assert call(topk=600) == ops.SA_ERR_UNSUPPORTED
     assert call(sc=float("nan")) == ops.SA_ERR_INVALID_ARG
-    assert call(S=-1) == ops.SA_ERR_INVALID_ARG
+    assert call(S=-2) == ops.SA_ERR_INVALID_ARG                        # below SA_SPLITS_FILL_GPU
+    assert call(S=-1, po=None, pl=None) == ops.SA_ERR_INVALID_ARG     # fill the GPU: 16 partitions need partials
     assert call(S=65) == ops.SA_ERR_UNSUPPORTED
     assert call(out=None) == ops.SA_ERR_INVALID_ARG                    # S == 1 needs out
     assert call(S=4, po=None, pl=P) == ops.SA_ERR_INVALID_ARG         # S > 1 needs partials
