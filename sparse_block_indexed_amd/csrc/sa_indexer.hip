@@ -16,16 +16,17 @@
 //               (v_dot2 bf16 -> fp32, eight lanes per key, DPP reduction);
 //               16 .. 63 rows take the 16-row MFMA scorer; 64 and more (a
 //               prefill chunk) the MFMA GEMM. One-byte E4M3 keys are widened
-//               to bf16 on the way in. The per-token scorer also lists, for
-//               each (row, chunk of blocks), its local candidates: every score
-//               at or above the histogram bin that holds the chunk's T-th
-//               largest score, in block order, with that bin's lower edge.
-//  2. select    (per-token scorer) per row: the exact k-th largest key tau_U of
+//               to bf16 on the way in. For histories over kFuseLimit blocks
+//               the per-token scorer also lists, for each (row, chunk of
+//               blocks), its local candidates: every score at or above the
+//               21-bit key prefix that holds the chunk's T-th largest score,
+//               in block order, with that prefix's lower edge.
+//  2. select    (histories over kFuseLimit) per row: the exact k-th largest key tau_U of
 //               the union of the row's candidate lists; a chunk whose edge lies
 //               above tau_U may hold unlisted keys >= tau_U and is re-read from
 //               its stored scores; the top k of everything >= tau_U (ties at
 //               the k-th key taken in block order) are written ascending.
-//     finalize  (MFMA scorers) per row: histogram of the top 11 key bits from
+//     finalize  (histories up to kFuseLimit) per row: histogram of the top 11 key bits from
 //               register-held scores, everything above the threshold bin is
 //               chosen; within the threshold bin the needed keys are taken by
 //               rank (larger key, then lower block id) or, for large bins, by
@@ -221,7 +222,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 // Score one step for NQ query tokens. Lane q8 of a block's octet holds the
 // 16-byte chunks q8 + 8i of the key: for bf16 keys 8 dims each (i < 4), for fp8
 // keys 16 dims each (i < 2), converted to bf16 pairs before the v_dot2.
-template <int NQ, bool kFp8>
+template <int NQ, bool kCand, bool kFp8>
 __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslot, const int* ncb,
                                            const u32x4* s_q, const u32x4 (&kv)[KeyFmt<kFp8>::kLoads], int beta,
                                            bool in, bool ok, int q8, uint32_t (*s_hist)[kHistBins],
@@ -258,8 +259,11 @@ __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslo
     }
     s = octet_sum(s);
     sc[j] = ok ? s : -INFINITY;   // an unreadable page ranks last
-    // the chunk's histogram of the top 11 key bits (lane j of the octet adds row j's score)
-    if (in && q8 == j && beta < ncb[j]) atomicAdd(&s_hist[hslot[j]][score_key(sc[j]) >> 21], 1u);
+    // candidate lists: the chunk's histogram of the top 11 key bits (lane j of
+    // the octet adds row j's score)
+    if constexpr (kCand) {
+      if (in && q8 == j && beta < ncb[j]) atomicAdd(&s_hist[hslot[j]][score_key(sc[j]) >> 21], 1u);
+    }
   }
 }
 
@@ -272,7 +276,7 @@ __device__ __forceinline__ void score_step(const IndexerArgs& a, const int* hslo
 // other buffers' loads in flight. After a group, lane (octet b, q8 < 4) holds
 // the scores of block 8*q8 + b of the group, so one store per token writes 32
 // consecutive scores (a whole 128-byte line).
-template <int NQ, bool kFp8>
+template <int NQ, bool kCand, bool kFp8>
 __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot, const int* ncb, int lo, int hi,
                           const int32_t* s_pages, const u32x4* s_q, uint32_t (*s_hist)[kHistBins],
                           float (*s_sc)[kCandChunkMax]) {
@@ -309,19 +313,19 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
   fill(k3, base + 24 + sub, in3, ok3);
   for (int g = 0; g < ngroups; ++g, base += 32) {
     float keep[NQ], sc[NQ];
-    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k0, base + sub, in0, ok0, q8, s_hist, sc);
+    score_step<NQ, kCand, kFp8>(a, hslot, ncb, s_q, k0, base + sub, in0, ok0, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = sc[j];
     fill(k0, base + 32 + sub, in0, ok0);
-    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k1, base + 8 + sub, in1, ok1, q8, s_hist, sc);
+    score_step<NQ, kCand, kFp8>(a, hslot, ncb, s_q, k1, base + 8 + sub, in1, ok1, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 1 ? sc[j] : keep[j];
     fill(k1, base + 40 + sub, in1, ok1);
-    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k2, base + 16 + sub, in2, ok2, q8, s_hist, sc);
+    score_step<NQ, kCand, kFp8>(a, hslot, ncb, s_q, k2, base + 16 + sub, in2, ok2, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 2 ? sc[j] : keep[j];
     fill(k2, base + 48 + sub, in2, ok2);
-    score_step<NQ, kFp8>(a, hslot, ncb, s_q, k3, base + 24 + sub, in3, ok3, q8, s_hist, sc);
+    score_step<NQ, kCand, kFp8>(a, hslot, ncb, s_q, k3, base + 24 + sub, in3, ok3, q8, s_hist, sc);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) keep[j] = q8 == 3 ? sc[j] : keep[j];
     fill(k3, base + 56 + sub, in3, ok3);
@@ -331,7 +335,7 @@ __device__ void score_run(const IndexerArgs& a, const int* tok, const int* hslot
       for (int j = 0; j < NQ; ++j) {
         if (beta < ncb[j]) {
           a.scores[(size_t)tok[j] * a.max_hist_blocks + beta] = keep[j];
-          s_sc[hslot[j]][beta - lo] = keep[j];
+          if constexpr (kCand) s_sc[hslot[j]][beta - lo] = keep[j];
         }
       }
     }
@@ -406,15 +410,17 @@ __device__ void emit_chunk_candidates(const IndexerArgs& a, int row, int chunk, 
 
 // Runs of up to GS query tokens of one sequence share a pass over its keys; GS
 // is the host's group size, so a one-token decode does not pay for four query
-// register sets. The workgroup's chunk of every row is kept in LDS (scores and
-// their histogram) and listed as local candidates at the end.
+// register sets. With kCand (histories over kFuseLimit blocks) the
+// workgroup's chunk of every row is kept in LDS (scores and their histogram)
+// and listed as local candidates at the end; shorter rows are selected by
+// finalize from their stored scores.
 static_assert(kMaxGroup == 4 && kMaxGroup * (kKeyBytes / 16) <= kThreads, "one index-query load per thread");
 static_assert(kCandChunkMax % (4 * kThreads) == 0, "whole float4 reads of a chunk row");
 
-template <int GS, bool kFp8>
+template <int GS, bool kCand, bool kFp8>
 __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
-  __shared__ __align__(16) uint32_t s_hist[GS][kHistBins];
-  __shared__ __align__(16) float s_sc[GS][kCandChunkMax];
+  __shared__ __align__(16) uint32_t s_hist[kCand ? GS : 1][kCand ? kHistBins : 4];
+  __shared__ __align__(16) float s_sc[kCand ? GS : 1][kCand ? kCandChunkMax : 4];
   __shared__ int32_t s_pages[kPagePasses * kThreads];   // page ids of the current run's blocks (padded)
   __shared__ u32x4 s_q[kThreads];   // index queries of the current run (padded)
   __shared__ uint32_t s_tmp[kThreads / 64];
@@ -439,8 +445,12 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
   for (int j = 0; j < ng; ++j) any |= ncb[j] > lo;
   if (!any) return;
 
-  for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) (&s_hist[0][0])[i] = 0u;
+  if constexpr (kCand)
+    for (int i = threadIdx.x; i < ng * kHistBins; i += kThreads) (&s_hist[0][0])[i] = 0u;
 
+  // (without kCand the row arrays are stand-ins that are never touched)
+  uint32_t (*hist_rows)[kHistBins] = reinterpret_cast<uint32_t (*)[kHistBins]>(&s_hist[0][0]);
+  float (*sc_rows)[kCandChunkMax] = reinterpret_cast<float (*)[kCandChunkMax]>(&s_sc[0][0]);
   uint32_t done = 0;
   for (int j0 = 0; j0 < ng; ++j0) {
     if ((done >> j0) & 1u) continue;
@@ -475,11 +485,12 @@ __global__ __launch_bounds__(kThreads) void score_kernel(IndexerArgs a) {
 #pragma unroll
     for (int r = 0; r < kPagePasses; ++r) s_pages[threadIdx.x + r * kThreads] = pg[r];
     __syncthreads();
-    if (nq == 1) score_run<1, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc);
-    if constexpr (GS >= 2) { if (nq == 2) score_run<2, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc); }
-    if constexpr (GS >= 3) { if (nq == 3) score_run<3, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc); }
-    if constexpr (GS >= 4) { if (nq == 4) score_run<4, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, s_hist, s_sc); }
+    if (nq == 1) score_run<1, kCand, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, hist_rows, sc_rows);
+    if constexpr (GS >= 2) { if (nq == 2) score_run<2, kCand, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, hist_rows, sc_rows); }
+    if constexpr (GS >= 3) { if (nq == 3) score_run<3, kCand, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, hist_rows, sc_rows); }
+    if constexpr (GS >= 4) { if (nq == 4) score_run<4, kCand, kFp8>(a, tok, hslot, cbs, lo, hi, s_pages, s_q, hist_rows, sc_rows); }
   }
+  if constexpr (!kCand) return;
   __syncthreads();
   // each row's local candidates of this chunk
   for (int j = 0; j < ng; ++j) {
@@ -1168,6 +1179,64 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
   emit_selection(sel_bm, eq_bm, need_eq, ncand, k, out, s.tmp, reinterpret_cast<int32_t*>(s.tz));
 }
 
+// Exact k-th largest (1 <= k <= m) of key_at(0 .. m-1), for key sets that are
+// small and crowded (the high end of a row): the bins of each radix level span
+// the keys' own range [lo, hi] (2048 bins of 2^sh keys, sh = bit width of the
+// range less 11), so that the first level spreads the keys over many bins and
+// the later levels (at most two more) only see the keys of the chosen bin.
+// *count_gt receives how many keys are strictly larger. NT threads.
+template <int NT, typename KeyAt>
+__device__ uint32_t radix_kth_range(KeyAt key_at, int m, uint32_t k, uint32_t* h, uint32_t* tmp, uint32_t* res,
+                                    uint32_t* count_gt) {
+  // range of the keys (wave reductions, then across the waves)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = threadIdx.x; i < m; i += NT) {
+    const uint32_t x = key_at(i);
+    kmin = min(kmin, x);
+    kmax = max(kmax, x);
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();   // tmp may still be read by an earlier scan
+  if ((threadIdx.x & 63) == 0) {
+    tmp[wave] = kmin;
+    tmp[NT / 64 + wave] = kmax;
+  }
+  __syncthreads();
+  kmin = tmp[0];
+  kmax = tmp[NT / 64];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) {
+    kmin = min(kmin, tmp[w]);
+    kmax = max(kmax, tmp[NT / 64 + w]);
+  }
+  __syncthreads();
+  uint32_t base = kmin;                                     // window [base, base + 2^width)
+  int width = kmax > kmin ? 32 - __clz(kmax - kmin) : 0;    // kmax - kmin < 2^width
+  uint32_t above = 0;
+  while (width > 0) {   // (uniform)
+    const int sh = max(0, width - 11);
+    for (int i = threadIdx.x; i < kHistBins; i += NT) h[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < m; i += NT) {
+      const uint32_t d = key_at(i) - base;   // (wraps to a large value below the window)
+      if (key_at(i) >= base && (width >= 32 || d < (1u << width))) atomicAdd(&h[d >> sh], 1u);
+    }
+    __syncthreads();
+    select_bin<NT>(h, kHistBins, k - above, tmp, res);
+    base += res[0] << sh;
+    above += res[1];
+    width = sh;
+    __syncthreads();
+  }
+  *count_gt = above;
+  return base;
+}
+
 // ---------------------------------------------------------------------------
 // 4. select (after the per-token scorer)
 // ---------------------------------------------------------------------------
@@ -1228,6 +1297,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   const int t = blockIdx.x;
   const int k = a.topk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int C = a.chunk_blocks;
+  const int nck_all = (a.max_hist_blocks + C - 1) / C;
+  const uint2* meta = a.cand_meta + (size_t)t * nck_all;
+  // the row's (count, edge) pairs are read together with its location (the
+  // reads are clamped into the row; pairs past the row's chunks are dropped)
+  uint2 mv[kSelChunksPer];
+#pragma unroll
+  for (int r = 0; r < kSelChunksPer; ++r)
+    mv[r] = meta[min((int)threadIdx.x * kSelChunksPer + r, min(nck_all, kSelMaxChunks) - 1)];
   int b, p;
   const int ncand = min(located_blocks(a, t, &b, &p), a.max_hist_blocks);
   const int len = seq_len_of(a, b);
@@ -1238,22 +1316,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = i < nv ? i : -1;
     return;
   }
-  const int C = a.chunk_blocks;
-  const int nck_all = (a.max_hist_blocks + C - 1) / C;
   const int nck = (ncand + C - 1) / C;
   if (nck > kSelMaxChunks) {
     select_ordered_global<kSelThreads>(a, s.h, s.tmp, s.res, t, ncand, out);
     return;
   }
-  const uint2* meta = a.cand_meta + (size_t)t * nck_all;
   const uint2* lists = a.cand + (size_t)t * a.cand_row_stride;
   const float* srow = a.scores + (size_t)t * a.max_hist_blocks;
 
   // 1. list lengths and edges; first entry of every list in U
-  for (int c = threadIdx.x; c < nck; c += kSelThreads) {
-    const uint2 m = meta[c];
-    s.off[c] = m.x;
-    s.edge[c] = m.y;
+#pragma unroll
+  for (int r = 0; r < kSelChunksPer; ++r) {
+    const int c = (int)threadIdx.x * kSelChunksPer + r;
+    if (c < nck) {
+      s.off[c] = mv[r].x;
+      s.edge[c] = mv[r].y;
+    }
   }
   __syncthreads();
   chunk_scan(s.off, nck, s.tmp);
@@ -1278,7 +1356,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   uint32_t tau = 0;
   if (m_u >= (uint32_t)k) {
     const uint32_t* keys = s.key;
-    tau = radix_kth<kSelThreads>([keys](int i) { return keys[i]; }, (int)m_u, (uint32_t)k, s.h, s.tmp, s.res, &gt);
+    tau = radix_kth_range<kSelThreads>([keys](int i) { return keys[i]; }, (int)m_u, (uint32_t)k, s.h, s.tmp, s.res,
+                                        &gt);
   }
   // 4. chunks that may hold unlisted keys >= tau_U
   bool mine = m_u < (uint32_t)k;
@@ -1345,7 +1424,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     __syncthreads();
     fkey = s.fkey;
     fid = s.fid;
-    tau = radix_kth<kSelThreads>([fkey](int i) { return fkey[i]; }, (int)mf, (uint32_t)k, s.h, s.tmp, s.res, &gt);
+    tau = radix_kth_range<kSelThreads>([fkey](int i) { return fkey[i]; }, (int)mf, (uint32_t)k, s.h, s.tmp, s.res,
+                                        &gt);
   }
   // 5. keys above tau, then keys equal to tau in block order until k are
   // taken; thread i owns entries kSelPer*i .. +kSelPer of F (or of U)
@@ -1397,10 +1477,11 @@ IndexerWorkspace indexer_workspace_layout(int n_tok, int max_pages_per_seq) {
   IndexerWorkspace w;
   const size_t nt = (size_t)(n_tok > 0 ? n_tok : 0);
   const int mhb = (max_pages_per_seq > 0 ? max_pages_per_seq : 0) * kBlocksPerPage;
+  const bool lists = mhb > kFuseLimit;   // candidate lists only for histories the finalize cannot hold
   w.scores_off = 0;
   w.meta_off = up(nt * (size_t)mhb * 4);
-  w.cand_off = w.meta_off + up(nt * (size_t)((mhb + 63) / 64) * 8);   // chunks are at least 64 blocks
-  w.total = w.cand_off + up(nt * indexer_cand_row_bound(mhb) * 8);
+  w.cand_off = w.meta_off + (lists ? up(nt * (size_t)((mhb + 63) / 64) * 8) : 0);   // chunks are at least 64 blocks
+  w.total = w.cand_off + (lists ? up(nt * indexer_cand_row_bound(mhb) * 8) : 0);
   return w;
 }
 
@@ -1433,10 +1514,18 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
   const int ngroups = (a.n_tok + a.group_size - 1) / a.group_size;
   const int nchunk = (a.max_hist_blocks + a.chunk_blocks - 1) / a.chunk_blocks;
   const dim3 sgrid((unsigned)((long long)ngroups * nchunk));
-#define SA_SCORE(GS)                                                                            \
-  do {                                                                                          \
-    if (a.key_fp8) score_kernel<GS, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);             \
-    else score_kernel<GS, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);                      \
+  // Histories up to kFuseLimit blocks: finalize selects from the stored scores
+  // (held in registers); longer ones: candidate lists and the select pass.
+  const bool lists = a.max_hist_blocks > kFuseLimit;
+#define SA_SCORE(GS)                                                                                 \
+  do {                                                                                               \
+    if (lists) {                                                                                     \
+      if (a.key_fp8) score_kernel<GS, true, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);          \
+      else score_kernel<GS, true, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);                   \
+    } else {                                                                                         \
+      if (a.key_fp8) score_kernel<GS, false, true><<<sgrid, dim3(kThreads), 0, stream>>>(a);         \
+      else score_kernel<GS, false, false><<<sgrid, dim3(kThreads), 0, stream>>>(a);                  \
+    }                                                                                                \
   } while (0)
   switch (a.group_size) {
     case 1: SA_SCORE(1); break;
@@ -1445,7 +1534,8 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t stream) {
     default: SA_SCORE(4); break;
   }
 #undef SA_SCORE
-  select_kernel<<<dim3((unsigned)a.n_tok), dim3(kSelThreads), 0, stream>>>(a);
+  if (lists) select_kernel<<<dim3((unsigned)a.n_tok), dim3(kSelThreads), 0, stream>>>(a);
+  else finalize_kernel<<<dim3((unsigned)a.n_tok), dim3(kFinalThreads), (size_t)a.bitmap_words * 2 * 4, stream>>>(a);
   return hipGetLastError();
 }
 

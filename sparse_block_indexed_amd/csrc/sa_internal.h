@@ -22,7 +22,7 @@ constexpr int kKeyBytes = kIdxDim * 2;                     // one index key
 
 // indexer workspace
 constexpr int kHistBins = 2048;       // first radix digit: key bits 31..21
-constexpr int kFuseLimit = 16384;     // longest history the MFMA scorers' finalize holds in registers
+constexpr int kFuseLimit = 16384;     // longest history finalize holds in registers (longer: candidate lists)
 constexpr int kCandChunkMax = 2048;   // longest block chunk of one per-token score workgroup
 constexpr int kChunkCap = 512;        // candidates one (row, chunk) may list
 

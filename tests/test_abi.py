@@ -54,13 +54,15 @@ def test_workspace_size(lib):
     c = lib.sa_indexer_topk_workspace_size(2, 256, 512)
     assert 0 < a < b < c
     assert a % 256 == 0
-    # per token: scores (4 B per historical block), one (count, edge) pair per
-    # chunk of at least 64 blocks, and candidate lists (8 B per entry) for every
-    # chunk length the host may pick: up to 512 entries per chunk, at most the chunk
-    blocks = 128 * 8
+    # per token: scores (4 B per historical block)
+    assert a >= 128 * 8 * 4
+    # histories over 16,384 blocks also hold, per token, one (count, edge) pair
+    # per chunk of at least 64 blocks and candidate lists (8 B per entry) for
+    # every chunk length the host may pick: up to 512 entries per chunk, at most the chunk
+    blocks = 16384 * 8
     lists = max(-(-blocks // c) * min(c, 512) for c in (64, 128, 256, 512, 1024, 2048))
     assert lists == blocks
-    assert a >= blocks * 4 + (blocks // 64) * 8 + lists * 8
+    assert lib.sa_indexer_topk_workspace_size(1, 16384, 512) >= blocks * 4 + (blocks // 64) * 8 + lists * 8
     # the 128K verify batch fits the no-alloc entry point's scratch array
     assert lib.sa_indexer_topk_workspace_size(256, 2048, 512) <= 64 << 20
 
