@@ -1184,7 +1184,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(IndexerArgs a) 
 // the keys' own range [lo, hi] (2048 bins of 2^sh keys, sh = bit width of the
 // range less 11), so that the first level spreads the keys over many bins and
 // the later levels (at most two more) only see the keys of the chosen bin.
-// *count_gt receives how many keys are strictly larger. NT threads.
+// After each level the keys of the chosen bin are checked for being one value
+// (scores of integer data are: their neighbours lie far apart in key space),
+// which ends the search there. *count_gt receives how many keys are strictly
+// larger. NT threads.
 template <int NT, typename KeyAt>
 __device__ uint32_t radix_kth_range(KeyAt key_at, int m, uint32_t k, uint32_t* h, uint32_t* tmp, uint32_t* res,
                                     uint32_t* count_gt) {
@@ -1231,7 +1234,33 @@ __device__ uint32_t radix_kth_range(KeyAt key_at, int m, uint32_t k, uint32_t* h
     base += res[0] << sh;
     above += res[1];
     width = sh;
+    if (width == 0) break;
+    // does the chosen bin [base, base + 2^width) hold a single key value?
+    uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
+    for (int i = threadIdx.x; i < m; i += NT) {
+      const uint32_t x = key_at(i);
+      if (x >= base && (width >= 32 || x - base < (1u << width))) {
+        bmin = min(bmin, x);
+        bmax = max(bmax, x);
+      }
+    }
+    if (threadIdx.x == 0) {
+      tmp[0] = 0xFFFFFFFFu;
+      tmp[1] = 0u;
+    }
     __syncthreads();
+    if (bmin != 0xFFFFFFFFu) {
+      atomicMin(&tmp[0], bmin);
+      atomicMax(&tmp[1], bmax);
+    }
+    __syncthreads();
+    bmin = tmp[0];
+    bmax = tmp[1];
+    __syncthreads();
+    if (bmin == bmax) {   // (uniform) one value: it is the k-th largest
+      base = bmin;
+      break;
+    }
   }
   *count_gt = above;
   return base;
@@ -1255,6 +1284,7 @@ constexpr int kSelCap = 6144;                     // list entries of one row hel
 constexpr int kSelMaxChunks = 1024;               // chunks of one row
 constexpr int kSelPer = kSelCap / kSelThreads;    // entries per thread in the ordered pass
 constexpr int kSelChunksPer = kSelMaxChunks / kSelThreads;
+static_assert(kSelCap < (1 << 16), "the ordered pass packs two counts of F in 32 bits");
 
 struct alignas(16) SelectLds {
   uint32_t key[kSelCap];    // U: the row's lists in chunk (= block) order
@@ -1340,14 +1370,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     select_ordered_global<kSelThreads>(a, s.h, s.tmp, s.res, t, ncand, out);
     return;
   }
-  // 2. U in chunk order (a wave per list)
-  for (int c = wave; c < nck; c += kWaves) {
+  // 2. U in chunk order: thread i copies the lists of chunks i and i + 512,
+  // 16 entries (eight 16-byte loads, all issued before any is waited for) at a
+  // time; the lists start 16-byte aligned (capacities are multiples of 64)
+  for (int c = threadIdx.x; c < nck; c += kSelThreads) {
     const uint32_t o = s.off[c], n = s.off[c + 1] - o;
-    const uint2* src = lists + (size_t)c * a.cand_cap;
-    for (uint32_t j = lane; j < n; j += 64) {
-      const uint2 e = src[j];
-      s.key[o + j] = e.x;
-      s.id[o + j] = e.y;
+    const uint4* src = reinterpret_cast<const uint4*>(lists + (size_t)c * a.cand_cap);
+    for (uint32_t j0 = 0; j0 < n; j0 += 16) {
+      uint4 e[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) e[r] = src[min(j0 / 2 + r, (n - 1) / 2)];   // (clamped into the list)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t j = j0 + 2 * r;
+        if (j < n) {
+          s.key[o + j] = e[r].x;
+          s.id[o + j] = e[r].y;
+        }
+        if (j + 1 < n) {
+          s.key[o + j + 1] = e[r].z;
+          s.id[o + j + 1] = e[r].w;
+        }
+      }
     }
   }
   __syncthreads();
@@ -1428,37 +1472,35 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
                                         &gt);
   }
   // 5. keys above tau, then keys equal to tau in block order until k are
-  // taken; thread i owns entries kSelPer*i .. +kSelPer of F (or of U)
+  // taken; thread i owns entries kSelPer*i .. +kSelPer of F (or of U). One scan
+  // of packed (above, equal) counts places every entry: a chosen entry goes to
+  // (entries above tau before it) + min(entries equal to tau before it, need_eq).
   const uint32_t need_eq = (uint32_t)k - min(gt, (uint32_t)k);
   const int i0 = (int)threadIdx.x * kSelPer;
   uint32_t kk[kSelPer];
-  uint32_t n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i) {
-    kk[i] = i0 + i < (int)mf ? fkey[i0 + i] : 0u;
-    n_eq += (i0 + i < (int)mf && kk[i] == tau) ? 1u : 0u;
-  }
-  uint32_t tot;
-  uint32_t eq_seen = block_prefix_exclusive<kSelThreads>(n_eq, s.tmp, &tot);
-  uint32_t takes = 0, n_take = 0;
+  uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const bool in = i0 + i < (int)mf;
-    const bool eq = in && kk[i] == tau;
-    const bool take = (in && kk[i] > tau) || (eq && eq_seen < need_eq);
-    eq_seen += eq ? 1u : 0u;
-    takes |= take ? 1u << i : 0u;
-    n_take += take ? 1u : 0u;
+    kk[i] = in ? fkey[i0 + i] : 0u;
+    n_gt += (in && kk[i] > tau) ? 1u : 0u;
+    n_eq += (in && kk[i] == tau) ? 1u : 0u;
   }
-  uint32_t pos = block_prefix_exclusive<kSelThreads>(n_take, s.tmp, &tot);
+  uint32_t tot;
+  const uint32_t before = block_prefix_exclusive<kSelThreads>(n_gt | n_eq << 16, s.tmp, &tot);
+  uint32_t gt_before = before & 0xffffu, eq_before = before >> 16;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    if ((takes >> i) & 1u) {
-      if (pos < (uint32_t)k) out[pos] = (int32_t)fid[i0 + i];
-      ++pos;
-    }
+    const bool in = i0 + i < (int)mf;
+    const bool above_tau = in && kk[i] > tau;
+    const bool eq = in && kk[i] == tau;
+    const uint32_t pos = gt_before + min(eq_before, need_eq);
+    if ((above_tau || (eq && eq_before < need_eq)) && pos < (uint32_t)k) out[pos] = (int32_t)fid[i0 + i];
+    gt_before += above_tau ? 1u : 0u;
+    eq_before += eq ? 1u : 0u;
   }
-  for (int i = (int)min(tot, (uint32_t)k) + (int)threadIdx.x; i < k; i += kSelThreads) out[i] = -1;   // (never: tot = k)
+  const uint32_t taken = (tot & 0xffffu) + min(tot >> 16, need_eq);
+  for (int i = (int)min(taken, (uint32_t)k) + (int)threadIdx.x; i < k; i += kSelThreads) out[i] = -1;   // (never: k are taken)
 }
 
 }  // namespace
