@@ -269,6 +269,7 @@ def layer_group(args, wl, dev):
     lses = [torch.empty((n_tok, 64), **f32) for _ in layers]
     pw = (torch.empty((n_tok, Sw, 64, 192), **f32), torch.empty((n_tok, Sw, 64), **f32)) if Sw > 1 else (None, None)
     ps = (torch.empty((n_tok, Ss, 64, 192), **f32), torch.empty((n_tok, Ss, 64), **f32)) if Ss > 1 else (None, None)
+    ctr = ops.merge_counters(n_tok, dev) if max(Sw, Ss) > 1 and args.fused_merge else None
     sel = torch.empty((n_tok, topk), dtype=torch.int32, device=dev)
     ws = torch.empty(ops.indexer_workspace_size(n_tok, wl.max_pages_per_seq, topk), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -276,14 +277,14 @@ def layer_group(args, wl, dev):
     def swa(i):
         L = layers[i]
         ops.swa_decode(L.q, L.k_cache, L.v_cache, pt, sl, qs, qp, window, SCALE, num_splits=Sw, out=outs[i],
-                       out_lse=lses[i], part_o=pw[0], part_lse=pw[1])
+                       out_lse=lses[i], part_o=pw[0], part_lse=pw[1], merge_counters=ctr)
 
     def indexer():
         ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, topk, sel_idx=sel, workspace=ws)
 
     def sparse():
         ops.sparse_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, sel, SCALE, num_splits=Ss, out=outs[3],
-                          out_lse=lses[3], part_o=ps[0], part_lse=ps[1])
+                          out_lse=lses[3], part_o=ps[0], part_lse=ps[1], merge_counters=ctr)
 
     def run_group():
         for i in range(3):
@@ -308,9 +309,11 @@ def layer_group(args, wl, dev):
     count = {"swa_decode": 3, "indexer_topk": 1, "sparse_decode": 1}
     dominant = max(phase_ms, key=lambda k: count[k] * phase_ms[k])
     achieved = nbytes[dominant] / (phase_ms[dominant] * 1e-3) / 1e9
-    kname = {"swa_decode": "attention_kernel<true, bf16>%s (sa_swa_decode)" % (" + merge_kernel" if Sw > 1 else ""),
+    sep = ctr is None
+    kname = {"swa_decode": "attention_kernel<true, bf16>%s (sa_swa_decode)" % (" + merge_kernel" if Sw > 1 and sep else ""),
              "indexer_topk": "sa_indexer_topk (score_kernel + select)",
-             "sparse_decode": "attention_kernel<false, bf16>%s (sa_sparse_decode)" % (" + merge_kernel" if Ss > 1 else "")}
+             "sparse_decode": "attention_kernel<false, bf16>%s (sa_sparse_decode)"
+                              % (" + merge_kernel" if Ss > 1 and sep else "")}
     group_bytes = sum(count[k] * nbytes[k] for k in nbytes)
     # parity of the timed buffers: the first window layer and the sparse layer, a few tokens each
     _, w_refs = cpu_baseline(layers[0], None, window, budget_s=2.0, max_tokens=4)
@@ -365,6 +368,9 @@ def main():
     ap.add_argument("--layer-group", action="store_true",
                     help="one step = a hybrid layer group: 3 sliding-window layers + 1 sparse layer, each with its "
                          "own Q and caches over the workload's sequences")
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="split calls merge in the attention launch (the last partition of each token and group "
+                         "merges; counters zeroed once) instead of in a second launch")
     ap.add_argument("--eager", action="store_true",
                     help="issue every call from Python instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -426,6 +432,8 @@ def main():
     lse = torch.empty((n_tok, 64), dtype=torch.float32, device=dev)
     part_o = torch.empty((n_tok, S, 64, 192), dtype=torch.float32, device=dev) if S > 1 else None
     part_lse = torch.empty((n_tok, S, 64), dtype=torch.float32, device=dev) if S > 1 else None
+    # split calls merge in the same launch: arrival counters, zeroed once
+    ctr = ops.merge_counters(n_tok, dev) if S > 1 and args.fused_merge else None
     stream = torch.cuda.current_stream()
 
     def run_indexer():
@@ -434,10 +442,10 @@ def main():
     def run_attention():
         if window is None:
             ops.sparse_decode(wl.q, kc, vc, pt, sl, qs, qp, sel, SCALE, num_splits=S, out=out,
-                              out_lse=lse, part_o=part_o, part_lse=part_lse, **kv_kw)
+                              out_lse=lse, part_o=part_o, part_lse=part_lse, merge_counters=ctr, **kv_kw)
         else:
             ops.swa_decode(wl.q, kc, vc, pt, sl, qs, qp, window, SCALE, num_splits=S, out=out,
-                           out_lse=lse, part_o=part_o, part_lse=part_lse, **kv_kw)
+                           out_lse=lse, part_o=part_o, part_lse=part_lse, merge_counters=ctr, **kv_kw)
 
     def run_step():
         if window is None:
@@ -499,6 +507,7 @@ def main():
               "block_tokens": 8, "page_tokens": 64, "heads": "64q/4kv", "head_dim": 192, "num_splits": S}
     config["kv_cache"] = "fp8_e4m3" if args.fp8_kv else "bf16"
     config["launch"] = "eager" if args.eager else "hip_graph"
+    config["merge"] = None if S == 1 else ("in the attention launch" if args.fused_merge else "second launch")
     config["num_splits_request"] = {-1: "fill_gpu", 0: "by_length"}.get(args.num_splits, args.num_splits)
     # value: steps back to back with inputs resident in HBM and L2/MALL not flushed between steps
     config["cache"] = "warm"
@@ -533,7 +542,7 @@ def main():
         "algorithmic_flops": {"indexer_topk": idx_flops, ("swa_decode" if window else "sparse_decode"): attn_flops},
     }
     kname = "attention_kernel<%s, %s>%s (%s%s)" % ("true" if window else "false", "fp8" if args.fp8_kv else "bf16",
-                                                   " + merge_kernel" if S > 1 else "",
+                                                   " + merge_kernel" if S > 1 and not args.fused_merge else "",
                                                    "sa_swa_decode" if window else "sa_sparse_decode",
                                                    "_fp8kv" if args.fp8_kv else "")
     if name == PREFILL_WORKLOAD:

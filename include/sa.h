@@ -193,7 +193,7 @@ sa_status sa_indexer_topk_grouped(const void* q_idx, const void* k_idx_cache, in
  * call allocates nothing. Every other argument and the result are those of
  * sa_indexer_topk. Sizes whose workspace (sa_indexer_topk_workspace_size) is
  * larger than the array give SA_ERR_WORKSPACE (the 128K verify batch, 256 tokens
- * of 131,072-token histories, needs 26 MiB). All calls on one GPU share the
+ * of 131,072-token histories, needs 16 MiB). All calls on one GPU share the
  * array: calls that overlap on one GPU (other streams, other threads) race.
  */
 #define SA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
@@ -234,15 +234,24 @@ int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits);
  * part_o, part_lse  device fp32 [n_tok][S][64][192], [n_tok][S][64]; needed when
  *              S > 1, ignored (may be NULL) when S == 1. A partition with
  *              lse = -inf attended nothing and its part_o may hold anything
+ * merge_counters  device uint32 [n_tok][4] or NULL; used when S > 1 and out is
+ *              non-NULL: the last partition of each (token, group) to finish
+ *              merges the S partials in the same launch (partition order, the
+ *              arithmetic of sa_merge, so the result is the same bit for bit).
+ *              They must be zero before the first call that uses them, and
+ *              every such call leaves them zero (allocate and zero once; a
+ *              call with more tokens uses words no call has touched, still
+ *              zero). Calls that run at the same time need their own. NULL:
+ *              the merge is a second launch.
  * out          device bf16 [n_tok][64][192] (round to nearest even) or NULL;
- *              when S > 1 and out is non-NULL the merge is enqueued too, when
- *              out is NULL only the partitions are written
+ *              when S > 1 and out is non-NULL the merge is done too, when out
+ *              is NULL only the partitions are written
  * out_lse      device fp32 [n_tok][64] natural-log lse, or NULL
  */
 sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                            sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
                            const int32_t* sel_idx, int n_tok, int topk, float softmax_scale,
-                           int num_splits, float* part_o, float* part_lse, void* out,
+                           int num_splits, float* part_o, float* part_lse, uint32_t* merge_counters, void* out,
                            float* out_lse, hipStream_t stream);
 
 /*
@@ -260,7 +269,7 @@ sa_status sa_sparse_decode_grouped(const void* q, const void* k_cache, const voi
                                    int kv_format, float k_scale, float v_scale, sa_paged_desc pd,
                                    const int32_t* q_seq, const int32_t* q_pos,
                                    const int32_t* sel_idx, int n_tok, int topk, float softmax_scale,
-                                   int num_splits, float* part_o, float* part_lse, void* out,
+                                   int num_splits, float* part_o, float* part_lse, uint32_t* merge_counters, void* out,
                                    float* out_lse, hipStream_t stream);
 
 /*
@@ -273,7 +282,7 @@ sa_status sa_sparse_decode_grouped(const void* q, const void* k_cache, const voi
 sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
                         sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
                         int n_tok, int window, float softmax_scale, int num_splits,
-                        float* part_o, float* part_lse, void* out, float* out_lse,
+                        float* part_o, float* part_lse, uint32_t* merge_counters, void* out, float* out_lse,
                         hipStream_t stream);
 
 /*
@@ -294,14 +303,14 @@ sa_status sa_sparse_decode_fp8kv(const void* q, const void* k_cache_fp8, const v
                                  float k_scale, float v_scale, sa_paged_desc pd,
                                  const int32_t* q_seq, const int32_t* q_pos, const int32_t* sel_idx,
                                  int n_tok, int topk, float softmax_scale, int num_splits,
-                                 float* part_o, float* part_lse, void* out, float* out_lse,
+                                 float* part_o, float* part_lse, uint32_t* merge_counters, void* out, float* out_lse,
                                  hipStream_t stream);
 
 sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8,
                               float k_scale, float v_scale, sa_paged_desc pd,
                               const int32_t* q_seq, const int32_t* q_pos, int n_tok, int window,
                               float softmax_scale, int num_splits, float* part_o, float* part_lse,
-                              void* out, float* out_lse, hipStream_t stream);
+                              uint32_t* merge_counters, void* out, float* out_lse, hipStream_t stream);
 
 /*
  * Merge of per-partition results (SGLang blog, "Kernels from StepFun").

@@ -33,8 +33,8 @@ sa_status check_tokens(const int32_t* q_seq, const int32_t* q_pos) {
 
 sa_status decode_common(const void* q, const void* k_cache, const void* v_cache, const sa_paged_desc& pd,
                         const int32_t* q_seq, const int32_t* q_pos, int n_tok, float softmax_scale,
-                        int max_blocks, int num_splits, float* part_o, float* part_lse, void* out,
-                        float* out_lse, bool window_mode, const int32_t* sel_idx, int topk, int window,
+                        int max_blocks, int num_splits, float* part_o, float* part_lse, uint32_t* merge_counters,
+                        void* out, float* out_lse, bool window_mode, const int32_t* sel_idx, int topk, int window,
                         bool kv_fp8, float k_scale, float v_scale, bool sel_per_group, hipStream_t stream) {
   if (n_tok < 0 || num_splits < SA_SPLITS_FILL_GPU) return SA_ERR_INVALID_ARG;
   if (n_tok == 0) return SA_OK;
@@ -57,6 +57,7 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   if (part_o != nullptr && !aligned(part_o, 16)) return SA_ERR_INVALID_ARG;
   if (part_lse != nullptr && !aligned(part_lse, 4)) return SA_ERR_INVALID_ARG;
   if (out_lse != nullptr && !aligned(out_lse, 4)) return SA_ERR_INVALID_ARG;
+  if (merge_counters != nullptr && !aligned(merge_counters, 4)) return SA_ERR_INVALID_ARG;
 
   sa::AttnArgs a;
   a.q = static_cast<const uint8_t*>(q);
@@ -89,8 +90,13 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   a.part_lse = S > 1 ? part_lse : nullptr;
   a.out = S == 1 ? static_cast<uint16_t*>(out) : nullptr;
   a.out_lse = S == 1 ? out_lse : nullptr;
+  // split with counters: the last partition of each (token, group) merges in the same launch
+  const bool fused = S > 1 && out != nullptr && merge_counters != nullptr;
+  a.merge_counters = fused ? merge_counters : nullptr;
+  a.merge_out = fused ? static_cast<uint16_t*>(out) : nullptr;
+  a.merge_lse = fused ? out_lse : nullptr;
   if (sa::launch_attention(a, window_mode, stream) != hipSuccess) return SA_ERR_HIP;
-  if (S > 1 && out != nullptr) {
+  if (S > 1 && out != nullptr && !fused) {
     if (sa::launch_merge(part_o, part_lse, n_tok, S, sa::kHeads, sa::kHeadDim, static_cast<uint16_t*>(out),
                          out_lse, stream) != hipSuccess)
       return SA_ERR_HIP;
@@ -241,32 +247,32 @@ sa_status sa_indexer_topk_fp8(const void* q_idx, const void* k_idx_cache_fp8, sa
 sa_status sa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,
                            const int32_t* q_seq, const int32_t* q_pos, const int32_t* sel_idx, int n_tok,
                            int topk, float softmax_scale, int num_splits, float* part_o, float* part_lse,
-                           void* out, float* out_lse, hipStream_t stream) {
+                           uint32_t* merge_counters, void* out, float* out_lse, hipStream_t stream) {
   if (n_tok > 0) {
     if (sel_idx == nullptr || !aligned(sel_idx, 4)) return SA_ERR_INVALID_ARG;
     if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
   }
   return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
-                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, false, 1.f, 1.f, false, stream);
+                       part_o, part_lse, merge_counters, out, out_lse, false, sel_idx, topk, 0, false, 1.f, 1.f, false, stream);
 }
 
 sa_status sa_sparse_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8, float k_scale,
                                  float v_scale, sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
                                  const int32_t* sel_idx, int n_tok, int topk, float softmax_scale, int num_splits,
-                                 float* part_o, float* part_lse, void* out, float* out_lse, hipStream_t stream) {
+                                 float* part_o, float* part_lse, uint32_t* merge_counters, void* out, float* out_lse, hipStream_t stream) {
   if (n_tok > 0) {
     if (sel_idx == nullptr || !aligned(sel_idx, 4)) return SA_ERR_INVALID_ARG;
     if (topk < 1 || topk > SA_MAX_TOPK) return SA_ERR_UNSUPPORTED;
   }
   return decode_common(q, k_cache_fp8, v_cache_fp8, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
-                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, true, k_scale, v_scale, false,
+                       part_o, part_lse, merge_counters, out, out_lse, false, sel_idx, topk, 0, true, k_scale, v_scale, false,
                        stream);
 }
 
 sa_status sa_sparse_decode_grouped(const void* q, const void* k_cache, const void* v_cache, int kv_format,
                                    float k_scale, float v_scale, sa_paged_desc pd, const int32_t* q_seq,
                                    const int32_t* q_pos, const int32_t* sel_idx, int n_tok, int topk,
-                                   float softmax_scale, int num_splits, float* part_o, float* part_lse, void* out,
+                                   float softmax_scale, int num_splits, float* part_o, float* part_lse, uint32_t* merge_counters, void* out,
                                    float* out_lse, hipStream_t stream) {
   if (kv_format != SA_FORMAT_BF16 && kv_format != SA_FORMAT_FP8_E4M3) return SA_ERR_UNSUPPORTED;
   const bool fp8 = kv_format == SA_FORMAT_FP8_E4M3;
@@ -276,26 +282,26 @@ sa_status sa_sparse_decode_grouped(const void* q, const void* k_cache, const voi
     if (n_tok > kMaxGroupedTokens) return SA_ERR_UNSUPPORTED;
   }
   return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, topk + 1, num_splits,
-                       part_o, part_lse, out, out_lse, false, sel_idx, topk, 0, fp8, fp8 ? k_scale : 1.f,
+                       part_o, part_lse, merge_counters, out, out_lse, false, sel_idx, topk, 0, fp8, fp8 ? k_scale : 1.f,
                        fp8 ? v_scale : 1.f, true, stream);
 }
 
 sa_status sa_swa_decode(const void* q, const void* k_cache, const void* v_cache, sa_paged_desc pd,
                         const int32_t* q_seq, const int32_t* q_pos, int n_tok, int window, float softmax_scale,
-                        int num_splits, float* part_o, float* part_lse, void* out, float* out_lse,
+                        int num_splits, float* part_o, float* part_lse, uint32_t* merge_counters, void* out, float* out_lse,
                         hipStream_t stream) {
   if (n_tok > 0 && (window < 1 || window > SA_MAX_WINDOW)) return SA_ERR_UNSUPPORTED;
   return decode_common(q, k_cache, v_cache, pd, q_seq, q_pos, n_tok, softmax_scale, window / 8 + 2, num_splits,
-                       part_o, part_lse, out, out_lse, true, nullptr, 0, window, false, 1.f, 1.f, false, stream);
+                       part_o, part_lse, merge_counters, out, out_lse, true, nullptr, 0, window, false, 1.f, 1.f, false, stream);
 }
 
 sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void* v_cache_fp8, float k_scale,
                               float v_scale, sa_paged_desc pd, const int32_t* q_seq, const int32_t* q_pos,
                               int n_tok, int window, float softmax_scale, int num_splits, float* part_o,
-                              float* part_lse, void* out, float* out_lse, hipStream_t stream) {
+                              float* part_lse, uint32_t* merge_counters, void* out, float* out_lse, hipStream_t stream) {
   if (n_tok > 0 && (window < 1 || window > SA_MAX_WINDOW)) return SA_ERR_UNSUPPORTED;
   return decode_common(q, k_cache_fp8, v_cache_fp8, pd, q_seq, q_pos, n_tok, softmax_scale, window / 8 + 2,
-                       num_splits, part_o, part_lse, out, out_lse, true, nullptr, 0, window, true, k_scale, v_scale,
+                       num_splits, part_o, part_lse, merge_counters, out, out_lse, true, nullptr, 0, window, true, k_scale, v_scale,
                        false, stream);
 }
 

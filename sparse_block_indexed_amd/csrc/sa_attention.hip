@@ -30,6 +30,12 @@
 // Token order inside a chunk is chosen so that the rows of the score half-tiles
 // land in exactly the lanes the PV step needs them in (half s, row 4*j + r <->
 // block j, token 4*s + r).
+//
+// Split calls (S > 1) write one partial result per partition. With kMerge the
+// partitions of a (token, group) count their arrivals on an integer counter
+// once their partial is visible device-wide; the last to arrive resets the
+// counter and merges the S partials in partition order with exactly the
+// arithmetic of the merge kernel, so no second launch is needed.
 
 #include <type_traits>
 
@@ -90,6 +96,28 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Reductions over the 64 lanes as butterflies (DPP swaps inside rows of 16,
+// then row swaps): every lane ends with the same bits. The same order as the
+// merge kernel's, so a merge here gives its results bit for bit.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max64(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));    // quad_perm 1,0,3,2
+  v = fmaxf(v, dpp_move<0x4E>(v));    // quad_perm 2,3,0,1
+  v = fmaxf(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
+  return max_over_groups(v);
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  return sum_over_groups(v);
+}
+
 template <bool kStream>
 __device__ __forceinline__ u32x2 load8_kv(const uint8_t* p) {
   if constexpr (kStream) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
@@ -109,7 +137,69 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // kFp8: one-byte caches. A K unit is [3 dim-blocks][8 tokens][64 dims], a V
 // unit [192 dims][8 tokens] (8 bytes per dim); both are widened exactly to bf16
 // right before their MFMA.
-template <bool kWindow, bool kStream, bool kFp8>
+// Merge of the S partials of (token t, group g) into the output, by the
+// workgroup of the partition that arrived last: wave w computes the weights of
+// heads 4w .. 4w+3 (lane s holds partition s), then thread i accumulates dims
+// 4*((i % 16) + 16 j), j < 3, of head i / 16 over the partitions in order.
+__device__ void merge_group(const AttnArgs& a, int t, int g, int S, float* s_w /* [16][64] */,
+                            float* s_ml /* [16][2] */) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = g * kHeadsPerGroup + 4 * wave + i;
+    l[i] = lane < S ? a.part_lse[((size_t)t * S + lane) * kHeads + h] : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float M = wave_max64(l[i]);
+    const bool any = M != -INFINITY;
+    const float w = (any && l[i] != -INFINITY) ? __builtin_amdgcn_exp2f((l[i] - M) * kLog2e) : 0.f;
+    const float L = wave_sum64(w);
+    const int hl = 4 * wave + i;
+    s_w[hl * 64 + lane] = w;
+    if (lane == 0) {
+      s_ml[2 * hl] = M;
+      s_ml[2 * hl + 1] = L;
+    }
+  }
+  __syncthreads();
+  const int hl = tid >> 4;   // head of the group
+  const int head = g * kHeadsPerGroup + hl;
+  const float* obase = a.part_o + ((size_t)t * S * kHeads + head) * kHeadDim + 4 * (tid & 15);
+  const size_t sstride = (size_t)kHeads * kHeadDim;
+  f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    f32x4 v[16][3];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        v[u][j] = *reinterpret_cast<const f32x4*>(obase + (size_t)min(s0 + u, S - 1) * sstride + 64 * j);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      // a partition with no weight (empty, or past S) adds nothing
+      const float wgt = s0 + u < S ? s_w[hl * 64 + min(s0 + u, 63)] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) acc[j] = wgt != 0.f ? acc[j] + v[u][j] * wgt : acc[j];
+    }
+  }
+  const float M = s_ml[2 * hl], L = s_ml[2 * hl + 1];
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  uint16_t* orow = a.merge_out + ((size_t)t * kHeads + head) * kHeadDim + 4 * (tid & 15);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    uint2 o;
+    o.x = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
+    o.y = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
+    *reinterpret_cast<uint2*>(orow + 64 * j) = o;
+  }
+  if (a.merge_lse != nullptr && (tid & 15) == 0)
+    a.merge_lse[(size_t)t * kHeads + head] = L > 0.f ? M + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
+}
+
+template <bool kWindow, bool kStream, bool kFp8, bool kMerge>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   constexpr int kUnit = kFp8 ? kUnitBytes / 2 : kUnitBytes;
   __shared__ int32_t s_unit[kFillSlots];   // entries past the token's list are written and never read
@@ -454,9 +544,44 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     if (a.out_lse != nullptr && wave == 0 && lg == 0) a.out_lse[(size_t)t * kHeads + head] = lse;
   } else {
     float* orow = a.part_o + (((size_t)t * S + sp) * kHeads + head) * kHeadDim + 4 * lg + 48 * wave;
+    float* lrow = a.part_lse + ((size_t)t * S + sp) * kHeads + head;
+    if constexpr (!kMerge) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) *reinterpret_cast<f32x4*>(orow + 16 * j) = o[j] * inv;
-    if (wave == 0 && lg == 0) a.part_lse[((size_t)t * S + sp) * kHeads + head] = lse;
+      for (int j = 0; j < 3; ++j) *reinterpret_cast<f32x4*>(orow + 16 * j) = o[j] * inv;
+      if (wave == 0 && lg == 0) *lrow = lse;
+    } else {
+      // The partial is written with device-scope atomic stores, which are
+      // visible device-wide once they complete (no L2 write-back needed, as an
+      // ordinary store's would be); once every thread's stores have completed
+      // the partition counts its arrival. The last of the S partitions resets
+      // the counter for the next call, and after a device-scope acquire (an L2
+      // invalidate on its own XCD only) merges the S partials.
+      __shared__ uint32_t s_last;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const f32x4 v = o[j] * inv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __hip_atomic_store(reinterpret_cast<uint32_t*>(orow + 16 * j + r), __float_as_uint(v[r]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (wave == 0 && lg == 0)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(lrow), __float_as_uint(lse), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have completed
+      __syncthreads();                 // ... and every other thread's
+      if (tid == 0) {
+        uint32_t* ctr = a.merge_counters + (size_t)t * kGroups + g;
+        const uint32_t before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before == (uint32_t)(S - 1) ? 1u : 0u;
+        if (s_last) *ctr = 0u;   // every partition has counted: none touches it again in this call
+      }
+      __syncthreads();
+      if (s_last == 0u) return;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // s_o is free now: weights [16][64] and (M, L) per head
+      merge_group(a, t, g, S, reinterpret_cast<float*>(&s_o[0][0][0]), reinterpret_cast<float*>(&s_o[1][0][0]));
+    }
   }
 }
 
@@ -466,10 +591,16 @@ hipError_t launch_attention(const AttnArgs& a, bool window_mode, hipStream_t str
   if (a.n_tok == 0) return hipSuccess;
   const long long grid = (long long)a.n_tok * kGroups * a.num_splits;
   const dim3 g((unsigned)grid), b(kThreads);
-#define SA_ATTN(W, F)                                                         \
-  do {                                                                        \
-    if (a.stream_kv) attention_kernel<W, true, F><<<g, b, 0, stream>>>(a);    \
-    else attention_kernel<W, false, F><<<g, b, 0, stream>>>(a);               \
+  const bool merge = a.num_splits > 1 && a.merge_counters != nullptr;
+#define SA_ATTN(W, F)                                                                       \
+  do {                                                                                      \
+    if (merge) {                                                                            \
+      if (a.stream_kv) attention_kernel<W, true, F, true><<<g, b, 0, stream>>>(a);          \
+      else attention_kernel<W, false, F, true><<<g, b, 0, stream>>>(a);                     \
+    } else {                                                                                \
+      if (a.stream_kv) attention_kernel<W, true, F, false><<<g, b, 0, stream>>>(a);         \
+      else attention_kernel<W, false, F, false><<<g, b, 0, stream>>>(a);                    \
+    }                                                                                       \
   } while (0)
   if (window_mode) {
     if (a.kv_fp8) SA_ATTN(true, true);

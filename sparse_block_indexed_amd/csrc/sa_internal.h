@@ -52,6 +52,11 @@ struct AttnArgs {
   float* part_lse;
   uint16_t* out;            // used when num_splits == 1
   float* out_lse;
+  // num_splits > 1 with the merge in the same launch: per (token, group)
+  // arrival counters (zero on entry, left zero), and the merge's outputs
+  uint32_t* merge_counters;
+  uint16_t* merge_out;
+  float* merge_lse;
 };
 
 struct IndexerArgs {

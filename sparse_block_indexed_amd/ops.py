@@ -66,22 +66,22 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = i32
         fn.argtypes = [vp, vp, PagedDesc, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.sa_sparse_decode.restype = i32
-    lib.sa_sparse_decode.argtypes = [vp, vp, vp, PagedDesc, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp]
+    lib.sa_sparse_decode.argtypes = [vp, vp, vp, PagedDesc, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
     lib.sa_swa_decode.restype = i32
-    lib.sa_swa_decode.argtypes = [vp, vp, vp, PagedDesc, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp]
+    lib.sa_swa_decode.argtypes = [vp, vp, vp, PagedDesc, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
     lib.sa_sparse_decode_fp8kv.restype = i32
     lib.sa_sparse_decode_fp8kv.argtypes = [vp, vp, vp, f32, f32, PagedDesc, vp, vp, vp, i32, i32, f32, i32, vp, vp,
-                                           vp, vp, vp]
+                                           vp, vp, vp, vp]
     lib.sa_swa_decode_fp8kv.restype = i32
     lib.sa_swa_decode_fp8kv.argtypes = [vp, vp, vp, f32, f32, PagedDesc, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp,
-                                        vp]
+                                        vp, vp]
     lib.sa_indexer_topk_grouped_workspace_size.restype = sz
     lib.sa_indexer_topk_grouped_workspace_size.argtypes = [i32, i32, i32]
     lib.sa_indexer_topk_grouped.restype = i32
     lib.sa_indexer_topk_grouped.argtypes = [vp, vp, i32, PagedDesc, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.sa_sparse_decode_grouped.restype = i32
     lib.sa_sparse_decode_grouped.argtypes = [vp, vp, vp, i32, f32, f32, PagedDesc, vp, vp, vp, i32, i32, f32, i32,
-                                             vp, vp, vp, vp, vp]
+                                             vp, vp, vp, vp, vp, vp]
     lib.sa_indexer_topk_noalloc.restype = i32
     lib.sa_indexer_topk_noalloc.argtypes = [vp, vp, PagedDesc, vp, vp, i32, i32, vp, vp]
     lib.sa_merge.restype = i32
@@ -221,6 +221,21 @@ def _decode_buffers(n_tok, S, dev, out, out_lse, part_o, part_lse, want_out=True
     return out, out_lse, part_o, part_lse
 
 
+def merge_counters(n_tok: int, device) -> torch.Tensor:
+    """A zeroed counter buffer for split decode calls that merge in the same
+    launch (allocate once; every call leaves it zero)."""
+    return torch.zeros((max(n_tok, 1), G), dtype=torch.int32, device=device)
+
+
+def _counters(c, n_tok, dev):
+    if c is None:
+        return None
+    _need(c, "merge_counters", torch.int32, dev)
+    if c.dim() != 2 or c.shape[1] != G or c.shape[0] < n_tok:
+        raise ValueError(f"merge_counters: expected [>= {n_tok}][{G}] int32")
+    return _ptr(c)
+
+
 def _is_fp8(t) -> bool:
     return t.dtype in (torch.uint8, torch.float8_e4m3fn)
 
@@ -256,11 +271,14 @@ def _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos, k_scale, v_scale):
 def sparse_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, sel_idx, softmax_scale: float,
                   num_splits: int = 0, out=None, out_lse=None, part_o=None, part_lse=None,
                   partials_only: bool = False, stream=None, k_scale: Optional[float] = None,
-                  v_scale: Optional[float] = None):
+                  v_scale: Optional[float] = None, merge_counters=None):
     """Attention over selected + current blocks. Returns (out, out_lse) or, with
     partials_only, (part_o, part_lse) of the resolved number of splits. One-byte
     caches (with k_scale, v_scale) go to sa_sparse_decode_fp8kv. A sel_idx of
-    shape [n_tok][4][topk] (one set per KV group) goes to sa_sparse_decode_grouped."""
+    shape [n_tok][4][topk] (one set per KV group) goes to sa_sparse_decode_grouped.
+    merge_counters (int32 [>= n_tok][4], zero before first use, left zero) makes
+    a split call merge in the same launch; without them the merge is a second
+    launch."""
     lib = load_library()
     dev, n_tok, fp8, k_cache, v_cache = _check_attn_inputs(q, k_cache, v_cache, q_seq, q_pos, k_scale, v_scale)
     per_group = sel_idx.dim() == 3
@@ -271,7 +289,8 @@ def sparse_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, sel_i
     out, out_lse, part_o, part_lse = _decode_buffers(n_tok, S, dev, out, out_lse, part_o, part_lse,
                                                      want_out=not partials_only)
     tail = (pd, _ptr(q_seq), _ptr(q_pos), _ptr(sel_idx), n_tok, topk, float(softmax_scale), int(num_splits),
-            _ptr(part_o), _ptr(part_lse), None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
+            _ptr(part_o), _ptr(part_lse), _counters(merge_counters, n_tok, dev),
+            None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
     if per_group:
         name = "sa_sparse_decode_grouped"
         st = lib.sa_sparse_decode_grouped(_ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -290,7 +309,7 @@ def sparse_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, sel_i
 def swa_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, window: int, softmax_scale: float,
                num_splits: int = 0, out=None, out_lse=None, part_o=None, part_lse=None,
                partials_only: bool = False, stream=None, k_scale: Optional[float] = None,
-               v_scale: Optional[float] = None):
+               v_scale: Optional[float] = None, merge_counters=None):
     """Sliding-window attention over positions max(0, p - window + 1) .. p.
     One-byte caches (with k_scale, v_scale) go to sa_swa_decode_fp8kv."""
     lib = load_library()
@@ -300,7 +319,8 @@ def swa_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, window: 
     out, out_lse, part_o, part_lse = _decode_buffers(n_tok, S, dev, out, out_lse, part_o, part_lse,
                                                      want_out=not partials_only)
     tail = (pd, _ptr(q_seq), _ptr(q_pos), n_tok, int(window), float(softmax_scale), int(num_splits), _ptr(part_o),
-            _ptr(part_lse), None if partials_only else _ptr(out), _ptr(out_lse), _stream(stream))
+            _ptr(part_lse), _counters(merge_counters, n_tok, dev), None if partials_only else _ptr(out),
+            _ptr(out_lse), _stream(stream))
     if fp8:
         name = "sa_swa_decode_fp8kv"
         st = lib.sa_swa_decode_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale), *tail)
@@ -331,10 +351,11 @@ def merge(part_o, part_lse, out=None, out_lse=None, stream=None):
 
 def sparse_layer(q, q_idx, k_cache, v_cache, k_idx_cache, page_table, seq_lens, q_seq, q_pos,
                  softmax_scale: float, topk: int = MAX_TOPK, num_splits: int = 0, workspace=None, stream=None,
-                 k_scale: Optional[float] = None, v_scale: Optional[float] = None):
+                 k_scale: Optional[float] = None, v_scale: Optional[float] = None, merge_counters=None):
     """The sparse layer's whole decode step: indexer top-k, then attention (+ merge)."""
     sel = indexer_topk(q_idx, k_idx_cache, page_table, seq_lens, q_seq, q_pos, topk, workspace=workspace,
                        stream=stream)
     out, lse = sparse_decode(q, k_cache, v_cache, page_table, seq_lens, q_seq, q_pos, sel, softmax_scale,
-                             num_splits=num_splits, stream=stream, k_scale=k_scale, v_scale=v_scale)
+                             num_splits=num_splits, stream=stream, k_scale=k_scale, v_scale=v_scale,
+                             merge_counters=merge_counters)
     return sel, out, lse

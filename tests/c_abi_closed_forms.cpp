@@ -163,6 +163,10 @@ int main() {
   hip_ok(hipMalloc((void**)&d_part_lse, sizeof(float) * n_tok * S * H), "hipMalloc part_lse");
   hip_ok(hipMalloc((void**)&d_out, sizeof(uint16_t) * n_tok * H * D), "hipMalloc out");
   hip_ok(hipMalloc((void**)&d_lse, sizeof(float) * n_tok * H), "hipMalloc lse");
+  // arrival counters of split calls that merge in the same launch: zeroed once
+  uint32_t* d_ctr = nullptr;
+  hip_ok(hipMalloc((void**)&d_ctr, sizeof(uint32_t) * n_tok * 4), "hipMalloc counters");
+  hip_ok(hipMemset(d_ctr, 0, sizeof(uint32_t) * n_tok * 4), "hipMemset counters");
   const float scale = 1.f / sqrtf((float)D);
   // tokens 0 .. 3 are valid (token 4's sequence does not exist: zero output, lse = -inf)
   auto check_constant_v = [&](const char* what) {
@@ -177,25 +181,39 @@ int main() {
       }
     check(ok, what);
   };
-  check(sa_swa_decode(d_q, d_k, d_v, pd, d_qs, d_qp, n_tok, 0, scale, 1, nullptr, nullptr, d_out, d_lse,
+  check(sa_swa_decode(d_q, d_k, d_v, pd, d_qs, d_qp, n_tok, 0, scale, 1, nullptr, nullptr, nullptr, d_out, d_lse,
                       stream) != SA_OK,
         "window 0 is refused");
-  for (int splits = 1; splits <= S; splits += S - 1) {
-    char what[128];
+  // unsplit; split + merge launch; split merged in the same launch (twice:
+  // the counters must be back at zero after each call)
+  const int pass_splits[4] = {1, S, S, S};
+  for (int pass = 0; pass < 4; ++pass) {
+    const int splits = pass_splits[pass];
+    uint32_t* ctr = pass >= 2 ? d_ctr : nullptr;
+    const char* how = pass >= 2 ? " merged in the same launch" : "";
+    char what[160];
     hip_ok(hipMemset(d_out, 0xff, sizeof(uint16_t) * n_tok * H * D), "hipMemset out");
-    check(sa_swa_decode(d_q, d_k, d_v, pd, d_qs, d_qp, n_tok, 64, scale, splits, d_part_o, d_part_lse, d_out,
+    check(sa_swa_decode(d_q, d_k, d_v, pd, d_qs, d_qp, n_tok, 64, scale, splits, d_part_o, d_part_lse, ctr, d_out,
                         d_lse, stream) == SA_OK,
           "sa_swa_decode accepted");
     hip_ok(hipStreamSynchronize(stream), "sync window");
-    snprintf(what, sizeof(what), "window 64, %d partition(s): every head returns its group's constant V", splits);
+    snprintf(what, sizeof(what), "window 64, %d partition(s)%s: every head returns its group's constant V", splits,
+             how);
     check_constant_v(what);
     hip_ok(hipMemset(d_out, 0xff, sizeof(uint16_t) * n_tok * H * D), "hipMemset out");
     check(sa_sparse_decode(d_q, d_k, d_v, pd, d_qs, d_qp, d_sel, n_tok, topk, scale, splits, d_part_o,
-                           d_part_lse, d_out, d_lse, stream) == SA_OK,
+                           d_part_lse, ctr, d_out, d_lse, stream) == SA_OK,
           "sa_sparse_decode accepted");
     hip_ok(hipStreamSynchronize(stream), "sync sparse");
-    snprintf(what, sizeof(what), "sparse, %d partition(s): every head returns its group's constant V", splits);
+    snprintf(what, sizeof(what), "sparse, %d partition(s)%s: every head returns its group's constant V", splits, how);
     check_constant_v(what);
+  }
+  {
+    std::vector<uint32_t> ctr(n_tok * 4, 1);
+    hip_ok(hipMemcpy(ctr.data(), d_ctr, sizeof(uint32_t) * n_tok * 4, hipMemcpyDeviceToHost), "copy counters");
+    bool zero = true;
+    for (uint32_t c : ctr) zero &= c == 0;
+    check(zero, "split calls that merge in the same launch leave their counters at zero");
   }
 
   // ---- merge: weights 1/4 and 3/4 ---------------------------------------
@@ -238,6 +256,7 @@ int main() {
   hipFree(d_sel);
   hipFree(d_part_o);
   hipFree(d_part_lse);
+  hipFree(d_ctr);
   hipFree(d_out);
   hipFree(d_lse);
   hipStreamDestroy(stream);

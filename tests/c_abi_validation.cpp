@@ -75,8 +75,8 @@ int main() {
          "no-alloc indexer null q");
   expect(sa_indexer_topk_noalloc(P, P, d, PI, PI, -3, 512, PI, nullptr), SA_ERR_INVALID_ARG,
          "no-alloc indexer n_tok -3");
-  expect(sa_indexer_topk_noalloc(P, P, desc(64, 2048, 1 << 20), PI, PI, 1024, 512, PI, nullptr), SA_ERR_WORKSPACE,
-         "no-alloc indexer: 1024 tokens of 128K histories need more than the scratch array");
+  expect(sa_indexer_topk_noalloc(P, P, desc(64, 2048, 1 << 20), PI, PI, 1100, 512, PI, nullptr), SA_ERR_WORKSPACE,
+         "no-alloc indexer: 1,100 tokens of 128K histories need more than the scratch array");
   expect(sa_indexer_topk_workspace_size(256, 2048, 512) <= SA_NOALLOC_SCRATCH_BYTES, 1,
          "the 128K verify batch fits the scratch array");
 
@@ -93,48 +93,48 @@ int main() {
 
   // sparse decode
   const float sc = 0.07f;
-  expect(sa_sparse_decode(nullptr, nullptr, nullptr, d, PI, PI, nullptr, 0, 512, sc, 0, nullptr, nullptr, nullptr,
+  expect(sa_sparse_decode(nullptr, nullptr, nullptr, d, PI, PI, nullptr, 0, 512, sc, 0, nullptr, nullptr, nullptr, nullptr,
                           nullptr, nullptr),
          SA_OK, "sparse n_tok 0");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, nullptr, 4, 512, sc, 1, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, nullptr, 4, 512, sc, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_INVALID_ARG, "sparse null selection");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 600, sc, 1, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 600, sc, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "sparse topk 600");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, NAN, 1, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, NAN, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_INVALID_ARG, "sparse NaN scale");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, 65, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, 65, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "sparse 65 splits");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, nullptr, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr),
          SA_ERR_INVALID_ARG, "sparse unsplit without out");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, 4, nullptr, PF, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, 4, nullptr, PF, nullptr, P, nullptr, nullptr),
          SA_ERR_INVALID_ARG, "sparse split without partials");
-  expect(sa_sparse_decode(P, at(4), P, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, at(4), P, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_INVALID_ARG, "sparse misaligned K");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 1 << 22, 512, 0.1f, 1, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 1 << 22, 512, 0.1f, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "sparse grid limit");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 1 << 20, 512, 0.1f, 2, PF, PF, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 1 << 20, 512, 0.1f, 2, PF, PF, nullptr, P, nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "sparse merge grid limit");
-  expect(sa_sparse_decode_fp8kv(P, P, P, 0.f, 1.f, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, P, nullptr,
+  expect(sa_sparse_decode_fp8kv(P, P, P, 0.f, 1.f, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, nullptr, P, nullptr,
                                 nullptr),
          SA_ERR_INVALID_ARG, "fp8 KV zero scale");
-  expect(sa_sparse_decode_fp8kv(P, P, P, 1e30f, 1.f, d, PI, PI, PI, 4, 512, 1e30f, 1, nullptr, nullptr, P,
+  expect(sa_sparse_decode_fp8kv(P, P, P, 1e30f, 1.f, d, PI, PI, PI, 4, 512, 1e30f, 1, nullptr, nullptr, nullptr, P,
                                 nullptr, nullptr),
          SA_ERR_INVALID_ARG, "fp8 KV logit scale overflow");
-  expect(sa_sparse_decode_grouped(P, P, P, 3, 1.f, 1.f, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, P, nullptr,
+  expect(sa_sparse_decode_grouped(P, P, P, 3, 1.f, 1.f, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, nullptr, P, nullptr,
                                   nullptr),
          SA_ERR_UNSUPPORTED, "grouped decode KV format 3");
-  expect(sa_sparse_decode_grouped(P, P, P, 0, 1.f, 1.f, d, PI, PI, PI, 1 << 29, 512, sc, 1, nullptr, nullptr, P,
+  expect(sa_sparse_decode_grouped(P, P, P, 0, 1.f, 1.f, d, PI, PI, PI, 1 << 29, 512, sc, 1, nullptr, nullptr, nullptr, P,
                                   nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "grouped decode 2^29 tokens");
 
   // window decode and merge
-  expect(sa_swa_decode(P, P, P, d, PI, PI, 0, 512, 0.1f, 0, nullptr, nullptr, nullptr, nullptr, nullptr), SA_OK,
+  expect(sa_swa_decode(P, P, P, d, PI, PI, 0, 512, 0.1f, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), SA_OK,
          "window n_tok 0");
-  expect(sa_swa_decode(P, P, P, d, PI, PI, 2, 0, 0.1f, 1, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_swa_decode(P, P, P, d, PI, PI, 2, 0, 0.1f, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "window 0");
-  expect(sa_swa_decode(P, P, P, d, PI, PI, 2, 5000, 0.1f, 1, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_swa_decode(P, P, P, d, PI, PI, 2, 5000, 0.1f, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "window 5000");
-  expect(sa_swa_decode_fp8kv(P, P, P, 1.f, INFINITY, d, PI, PI, 2, 512, 0.1f, 1, nullptr, nullptr, P, nullptr,
+  expect(sa_swa_decode_fp8kv(P, P, P, 1.f, INFINITY, d, PI, PI, 2, 512, 0.1f, 1, nullptr, nullptr, nullptr, P, nullptr,
                              nullptr),
          SA_ERR_INVALID_ARG, "fp8 window infinite scale");
   expect(sa_merge(nullptr, nullptr, 0, 1, 64, 192, nullptr, nullptr, nullptr), SA_OK, "merge n_tok 0");
@@ -152,9 +152,9 @@ int main() {
   expect(sa_resolve_num_splits(1, 1 << 20, SA_SPLITS_BY_LENGTH), SA_MAX_SPLITS, "by length: clamped");
   expect(sa_resolve_num_splits(4, 513, 100), SA_MAX_SPLITS, "explicit count clamped");
   expect(sa_resolve_num_splits(4, 513, -7), 1, "another negative request");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, -2, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 4, 512, sc, -2, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_INVALID_ARG, "sparse num_splits -2");
-  expect(sa_swa_decode(P, P, P, d, PI, PI, 2, 512, 0.1f, -2, nullptr, nullptr, P, nullptr, nullptr),
+  expect(sa_swa_decode(P, P, P, d, PI, PI, 2, 512, 0.1f, -2, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_INVALID_ARG, "window num_splits -2");
   expect(strcmp(sa_status_string((sa_status)99), "SA_ERR_UNKNOWN") == 0, 1, "unknown status name");
 

@@ -126,12 +126,13 @@ def test_sparse_decode_validation(lib):
     from sparse_block_indexed_amd import ops
     d = _desc(ops)
     f = lib.sa_sparse_decode
-    ok = dict(q=P, k=P, v=P, qs=P, qp=P, sel=P, n=4, topk=512, sc=0.07, S=1, po=None, pl=None, out=P, ol=None)
+    ok = dict(q=P, k=P, v=P, qs=P, qp=P, sel=P, n=4, topk=512, sc=0.07, S=1, po=None, pl=None, ctr=None, out=P,
+              ol=None)
 
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["q"], a["k"], a["v"], d, a["qs"], a["qp"], a["sel"], a["n"], a["topk"], ctypes.c_float(a["sc"]),
-                 a["S"], a["po"], a["pl"], a["out"], a["ol"], None)
+                 a["S"], a["po"], a["pl"], a["ctr"], a["out"], a["ol"], None)
 
     assert call(n=0, q=None, k=None, v=None, sel=None, out=None) == ops.SA_OK
     assert call(n=-1) == ops.SA_ERR_INVALID_ARG
@@ -146,6 +147,7 @@ def test_sparse_decode_validation(lib):
     assert call(out=None) == ops.SA_ERR_INVALID_ARG                    # S == 1 needs out
     assert call(S=4, po=None, pl=P) == ops.SA_ERR_INVALID_ARG         # S > 1 needs partials
     assert call(k=P + 4) == ops.SA_ERR_INVALID_ARG                     # misaligned cache
+    assert call(S=4, po=P, pl=P, ctr=P + 2) == ops.SA_ERR_INVALID_ARG  # misaligned merge counters
 
 
 def test_fp8kv_decode_validation(lib):
@@ -158,7 +160,8 @@ def test_fp8kv_decode_validation(lib):
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["q"], a["k"], a["v"], ctypes.c_float(a["ks"]), ctypes.c_float(a["vs"]), d, a["qs"], a["qp"],
-                 a["sel"], a["n"], a["topk"], ctypes.c_float(a["sc"]), a["S"], None, None, a["out"], None, None)
+                 a["sel"], a["n"], a["topk"], ctypes.c_float(a["sc"]), a["S"], None, None, None, a["out"], None,
+                 None)
 
     assert call(n=0, q=None, k=None, v=None, sel=None, out=None) == ops.SA_OK
     for bad in (0.0, -1.0, float("nan"), float("inf")):
@@ -170,11 +173,11 @@ def test_fp8kv_decode_validation(lib):
     assert call(v=P + 8) == ops.SA_ERR_INVALID_ARG
     w = lib.sa_swa_decode_fp8kv
     assert w(P, P, P, ctypes.c_float(1.0), ctypes.c_float(1.0), d, P, P, 0, 512, ctypes.c_float(0.1), 0,
-             None, None, None, None, None) == ops.SA_OK
+             None, None, None, None, None, None) == ops.SA_OK
     assert w(P, P, P, ctypes.c_float(1.0), ctypes.c_float(0.0), d, P, P, 2, 512, ctypes.c_float(0.1), 1,
-             None, None, P, None, None) == ops.SA_ERR_INVALID_ARG
+             None, None, None, P, None, None) == ops.SA_ERR_INVALID_ARG
     assert w(P, P, P, ctypes.c_float(1.0), ctypes.c_float(1.0), d, P, P, 2, 0, ctypes.c_float(0.1), 1,
-             None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
+             None, None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
 
 
 def test_binding_checks_fp8_cache_arguments():
@@ -218,10 +221,11 @@ def test_grouped_entry_points_validation(lib):
     one = ctypes.c_float(1.0)
 
     def call(fmt=0, ks=one, vs=one, sel=P, n=4, topk=512, out=P):
-        return g(P, P, P, fmt, ks, vs, d, P, P, sel, n, topk, ctypes.c_float(0.07), 1, None, None, out, None, None)
+        return g(P, P, P, fmt, ks, vs, d, P, P, sel, n, topk, ctypes.c_float(0.07), 1, None, None, None, out, None,
+                 None)
 
     assert g(None, None, None, 0, one, one, d, None, None, None, 0, 512, ctypes.c_float(0.07), 0, None, None,
-             None, None, None) == ops.SA_OK
+             None, None, None, None) == ops.SA_OK
     assert call(fmt=3) == ops.SA_ERR_UNSUPPORTED
     assert call(sel=None) == ops.SA_ERR_INVALID_ARG
     assert call(topk=513) == ops.SA_ERR_UNSUPPORTED
@@ -239,9 +243,9 @@ def test_grid_limits_are_refused(lib):
     long_d = _desc(ops, max_pages=1 << 20, num_pages=1 << 20)                  # 8M-block histories
     assert lib.sa_indexer_topk(P, P, long_d, P, P, 1 << 16, 512, P, P, huge_ws, None) == ops.SA_ERR_UNSUPPORTED
     f = lib.sa_sparse_decode
-    assert f(P, P, P, d, P, P, P, 1 << 22, 512, ctypes.c_float(0.1), 1, None, None, P, None, None) \
+    assert f(P, P, P, d, P, P, P, 1 << 22, 512, ctypes.c_float(0.1), 1, None, None, None, P, None, None) \
         == ops.SA_ERR_UNSUPPORTED                                               # 2^22 tokens x 4 groups x 256
-    assert f(P, P, P, d, P, P, P, 1 << 20, 512, ctypes.c_float(0.1), 2, P, P, P, None, None) \
+    assert f(P, P, P, d, P, P, P, 1 << 20, 512, ctypes.c_float(0.1), 2, P, P, None, P, None, None) \
         == ops.SA_ERR_UNSUPPORTED                                               # the merge: 2^20 x 64 heads x 64
     assert lib.sa_merge(P, P, 1 << 20, 2, 64, 192, P, None, None) == ops.SA_ERR_UNSUPPORTED
 
@@ -250,9 +254,10 @@ def test_swa_and_merge_validation(lib):
     from sparse_block_indexed_amd import ops
     d = _desc(ops)
     f = lib.sa_swa_decode
-    assert f(P, P, P, d, P, P, 0, 512, ctypes.c_float(0.1), 0, None, None, None, None, None) == ops.SA_OK
-    assert f(P, P, P, d, P, P, 2, 0, ctypes.c_float(0.1), 1, None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
-    assert f(P, P, P, d, P, P, 2, 5000, ctypes.c_float(0.1), 1, None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, P, d, P, P, 0, 512, ctypes.c_float(0.1), 0, None, None, None, None, None, None) == ops.SA_OK
+    assert f(P, P, P, d, P, P, 2, 0, ctypes.c_float(0.1), 1, None, None, None, P, None, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, P, d, P, P, 2, 5000, ctypes.c_float(0.1), 1, None, None, None, P, None, None) \
+        == ops.SA_ERR_UNSUPPORTED
     m = lib.sa_merge
     assert m(None, None, 0, 1, 64, 192, None, None, None) == ops.SA_OK
     assert m(P, P, 2, 0, 64, 192, P, None, None) == ops.SA_ERR_INVALID_ARG
