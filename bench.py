@@ -45,26 +45,115 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 GRAPH_STEPS = 10          # steps per graph replay in the timed loop
 SCALE = 1.0 / math.sqrt(192.0)
-PMC_FILE = os.path.join(ROOT, "profiles", "attention_mtp_verify_128k_pmc.json")
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_block_indexed_amd", "csrc", "sa_attention.hip")
+CSRC = os.path.join(ROOT, "sparse_block_indexed_amd", "csrc")
+# the kernels of each timed phase, and the sources they are built from
+PHASE_KERNELS = {"indexer_topk": ("score_kernel", "score_gemm_kernel", "score_mfma_kernel", "select_kernel",
+                                  "finalize_kernel"),
+                 "sparse_decode": ("attention_kernel", "merge_kernel"),
+                 "swa_decode": ("attention_kernel", "merge_kernel")}
+PHASE_SOURCES = {"indexer_topk": ("sa_indexer.hip",), "sparse_decode": ("sa_attention.hip", "sa_merge.hip"),
+                 "swa_decode": ("sa_attention.hip", "sa_merge.hip")}
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def pmc_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
+
+
+def source_hash(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
-    or None if they are missing or were taken on a different kernel source."""
+def counter_traffic(workload: str, phase: str):
+    """HBM bytes per call of a phase from the committed rocprofv3 counter runs
+    of the workload, or None if there are none or they were taken on other
+    kernel sources."""
     try:
-        with open(PMC_FILE) as f:
+        with open(pmc_file(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if any(rec.get("source_sha256_16", {}).get(n) != source_hash(n) for n in PHASE_SOURCES[phase]):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("phases", {}).get(phase, {}).get("bytes_per_call")
+
+
+def _pmc_rows(directory: str, counter: str):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    per = {}
+    with open(files[0], newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [(name, v) for (_, name), v in per.items()]
+
+
+def write_pmc_record(args):
+    """profiles/pmc_<workload>.json from rocprofv3 --pmc runs of this benchmark
+    (FETCH_SIZE and WRITE_SIZE of the workload, the same two counters of the
+    1 GiB copy, and optional further counters): per phase, the counters of
+    each of its kernels averaged over their dispatches; HBM bytes per call =
+    FETCH_SIZE x the copy's read scale + WRITE_SIZE x its write scale, summed
+    over the phase's kernels (each call launches each of them once)."""
+    dirs = dict(x.split("=", 1) for x in args.pmc_dir)
+    copy = dict(x.split("=", 1) for x in args.pmc_copy)
+    one_gib_kib = float(1 << 20)
+    # the copies only (the run also fills the source buffer once)
+    cfs = [v for n, v in _pmc_rows(copy["FETCH_SIZE"], "FETCH_SIZE") if "copyBuffer" in n or "copy_kernel" in n]
+    cws = [v for n, v in _pmc_rows(copy["WRITE_SIZE"], "WRITE_SIZE") if "copyBuffer" in n or "copy_kernel" in n]
+    launches = 5   # bench.py --copy-calibration copies 1 GiB five times
+    if len(cfs) != launches or len(cws) != launches:
+        raise SystemExit(f"expected {launches} copy dispatches, found {len(cfs)} / {len(cws)}")
+    cf, cw = sum(cfs), sum(cws)
+    cal = {"bytes_read_per_copy": 1 << 30, "bytes_written_per_copy": 1 << 30, "copies": launches,
+           "fetch_size_kib_per_copy": cf / launches, "write_size_kib_per_copy": cw / launches,
+           "fetch_scale": one_gib_kib / (cf / launches), "write_scale": one_gib_kib / (cw / launches)}
+    phases = {}
+    for phase, kernels in PHASE_KERNELS.items():
+        ph = {}
+        for counter, d in dirs.items():
+            for name, v in _pmc_rows(d, counter):
+                short = next((k for k in kernels if f"::{k}" in name), None)
+                if short is None:
+                    continue
+                e = ph.setdefault(short, {}).setdefault(counter, [])
+                e.append(v)
+        if not ph:
+            continue
+        if phase == "swa_decode" and not args.workload.startswith("swa"):
+            continue
+        if phase == "sparse_decode" and args.workload.startswith("swa"):
+            continue
+        kern = {}
+        total = 0.0
+        for short, cs in ph.items():
+            kern[short] = {c: {"dispatches": len(v), "mean": sum(v) / len(v)} for c, v in cs.items()}
+            b = 0.0
+            if "FETCH_SIZE" in cs:
+                b += kern[short]["FETCH_SIZE"]["mean"] * 1024 * cal["fetch_scale"]
+            if "WRITE_SIZE" in cs:
+                b += kern[short]["WRITE_SIZE"]["mean"] * 1024 * cal["write_scale"]
+            kern[short]["hbm_bytes_per_launch"] = b
+            total += b
+        phases[phase] = {"kernels": kern, "bytes_per_call": int(round(total))}
+    rec = {"workload": args.workload,
+           "commands": {c: f"rocprofv3 --pmc {c} -d gpurun_out/pmc/{args.workload}_{c} -o bench --output-format csv "
+                           f"-- python3 bench.py --workload {args.workload} --eager --steps 3 --warmup 1 "
+                           f"--cold-steps 0 --no-cpu-baseline" for c in dirs},
+           "copy_calibration_command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d gpurun_out/pmc/copy_<counter> "
+                                       "-o copy --output-format csv -- python3 bench.py --copy-calibration",
+           "copy_calibration": cal, "phases": phases,
+           "source_sha256_16": {n: source_hash(n) for n in ("sa_indexer.hip", "sa_attention.hip", "sa_merge.hip")}}
+    with open(pmc_file(args.workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({k: v["bytes_per_call"] for k, v in phases.items()}))
 
 
 def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: int = 64, kv_fp8=None,
@@ -375,7 +464,16 @@ def main():
                     help="issue every call from Python instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
+    ap.add_argument("--pmc-record", action="store_true",
+                    help="host only: write profiles/pmc_<workload>.json from rocprofv3 --pmc output directories")
+    ap.add_argument("--pmc-dir", action="append", default=[], metavar="COUNTER=DIR",
+                    help="a --pmc run of this workload (FETCH_SIZE, WRITE_SIZE, further counters)")
+    ap.add_argument("--pmc-copy", action="append", default=[], metavar="COUNTER=DIR",
+                    help="a --pmc run of --copy-calibration (FETCH_SIZE and WRITE_SIZE)")
     args = ap.parse_args()
+    if args.pmc_record:
+        write_pmc_record(args)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
@@ -551,18 +649,21 @@ def main():
         result["mfma_utilisation"] = tf / (PEAK_BF16_TFLOPS)
         attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                              "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": kname}
+                              "frac": attn_tf / PEAK_BF16_TFLOPS,
+                              "traffic": None if tags else counter_traffic(name, "sparse_decode"), "kernel": kname}
     elif name == LONG_CONTEXT_WORKLOAD:
         # at 1M context the index-key scan is the dominant read
         achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                              "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
-                              "kernel": "sa_indexer_topk (score_kernel + select)"}
+                              "frac": achieved / PEAK_HBM_GBPS,
+                              "traffic": None if tags else counter_traffic(name, "indexer_topk"),
+                              "kernel": "sa_indexer_topk (score_kernel + select_kernel)"}
     else:
         achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                               "frac": achieved / PEAK_HBM_GBPS,
-                              "traffic": counter_traffic() if (name == HEADLINE and not tags) else None,
+                              "traffic": None if tags else counter_traffic(name, "swa_decode" if window
+                                                                           else "sparse_decode"),
                               "kernel": kname}
     if cold_ms is not None:
         result["cold_cache"] = {"ms_per_step": cold_ms, "query_tokens_per_s": n_tok / (cold_ms * 1e-3),
