@@ -78,6 +78,20 @@ def counter_traffic(workload: str, phase: str):
     return rec.get("phases", {}).get(phase, {}).get("bytes_per_call")
 
 
+def counter_mean(workload: str, phase: str, kernel: str, counter: str):
+    """Mean per dispatch of a further counter of one kernel from the committed
+    counter runs of the workload, or None (no such run, or other sources)."""
+    try:
+        with open(pmc_file(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if any(rec.get("source_sha256_16", {}).get(n) != source_hash(n) for n in PHASE_SOURCES[phase]):
+        return None
+    e = rec.get("phases", {}).get(phase, {}).get("kernels", {}).get(kernel, {}).get(counter)
+    return None if e is None else e["mean"]
+
+
 def _pmc_rows(directory: str, counter: str):
     """(kernel name, value) per dispatch from a rocprofv3 --pmc CSV directory."""
     import csv
@@ -432,6 +446,56 @@ def layer_group(args, wl, dev):
     }
 
 
+def ceilings(dev):
+    """Practical ceilings of this device, measured with torch's own kernels
+    (HIP events, medians): copy and read bandwidth, and the time per step of a
+    HIP graph whose steps are chains of n dependent one-element kernels (GRAPH_STEPS
+    steps per replay, as the timed loop replays them)."""
+    import torch
+
+    def med(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    res = {}
+    x = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    t = med(lambda: y.copy_(x))
+    res["copy_1gib"] = {"us": t * 1e6, "read_plus_write_gbps": 2 * (1 << 30) / t / 1e9}
+    del x, y
+    z = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    t = med(lambda: z.sum())
+    res["read_4gib_torch_sum"] = {"us": t * 1e6, "read_gbps": (4 << 30) / t / 1e9}
+    del z
+    one = torch.zeros(1, dtype=torch.float32, device=dev)
+    floor = {}
+    for n in (1, 2, 3, 4, 8):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(GRAPH_STEPS * n):
+                one.add_(1.0)
+        t = med(g.replay)
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            for _ in range(n):
+                one.add_(1.0)
+        t1 = med(g1.replay)
+        floor[str(n)] = {"us_per_step": t / GRAPH_STEPS * 1e6, "us_per_replay_of_one_step": t1 * 1e6}
+    res["graph_chain_floor"] = floor
+    res["how"] = ("medians of 20 timed calls; graph_chain_floor[n]: a graph of %d steps of n dependent "
+                  "one-element kernels (per step), and a graph of one such step (per replay)" % GRAPH_STEPS)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -464,6 +528,10 @@ def main():
                     help="issue every call from Python instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the device's practical ceilings: a 1 GiB device copy, a 4 GiB read "
+                         "(torch sum), and graphs of chains of 1 .. 8 one-element kernels (the launch floor of "
+                         "a step of that many dependent kernels)")
     ap.add_argument("--pmc-record", action="store_true",
                     help="host only: write profiles/pmc_<workload>.json from rocprofv3 --pmc output directories")
     ap.add_argument("--pmc-dir", action="append", default=[], metavar="COUNTER=DIR",
@@ -491,6 +559,10 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return
+
+    if args.ceilings:
+        print(json.dumps(ceilings(dev)), flush=True)
         return
 
     from sparse_block_indexed_amd import bytes_model as B
@@ -648,9 +720,17 @@ def main():
         tf = (attn_flops + idx_flops) / (ms_per_step * 1e-3) / 1e12
         result["mfma_utilisation"] = tf / (PEAK_BF16_TFLOPS)
         attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
+        traffic = None if tags else counter_traffic(name, "sparse_decode")
         result["roofline"] = {"bound": "mfma", "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                              "frac": attn_tf / PEAK_BF16_TFLOPS,
-                              "traffic": None if tags else counter_traffic(name, "sparse_decode"), "kernel": kname}
+                              "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kname}
+        if not tags:
+            # the MFMA counters of the same kernel (rocprofv3 --pmc MfmaUtil, MfmaFlopsBF16), and the rate of
+            # its counted HBM traffic: the gathered K/V, not the matrix cores, bound this kernel
+            util = counter_mean(name, "sparse_decode", "attention_kernel", "MfmaUtil")
+            flops = counter_mean(name, "sparse_decode", "attention_kernel", "MfmaFlopsBF16")
+            result["roofline"]["counters"] = {
+                "mfma_util_pct": util, "mfma_flops_bf16_per_launch": flops,
+                "hbm_traffic_gbps": None if traffic is None else traffic / (attn_ms * 1e-3) / 1e9}
     elif name == LONG_CONTEXT_WORKLOAD:
         # at 1M context the index-key scan is the dominant read
         achieved = idx_bytes / (idx_ms * 1e-3) / 1e9

@@ -48,9 +48,9 @@ sa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   if (num_splits > SA_MAX_SPLITS) return SA_ERR_UNSUPPORTED;
   const int S = sa_resolve_num_splits(n_tok, max_blocks, num_splits);
   // launch limits: fewer than 2^32 threads per grid (attention: 256 per
-  // (token, group, partition); merge: 64 per (token, head))
+  // (token, group, partition); merge: 256 per (token, head))
   if ((long long)n_tok * sa::kGroups * S * 256 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;
-  if (S > 1 && (long long)n_tok * sa::kHeads * 64 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;
+  if (S > 1 && (long long)n_tok * sa::kHeads * 256 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;
   if (S == 1 && out == nullptr) return SA_ERR_INVALID_ARG;
   if (S > 1 && (part_o == nullptr || part_lse == nullptr)) return SA_ERR_INVALID_ARG;
   if (out != nullptr && !aligned(out, 16)) return SA_ERR_INVALID_ARG;
@@ -315,7 +315,7 @@ sa_status sa_merge(const float* part_o, const float* part_lse, int n_tok, int nu
     return SA_ERR_UNSUPPORTED;
   if (!aligned(part_o, 16) || !aligned(part_lse, 4) || !aligned(out, 8)) return SA_ERR_INVALID_ARG;
   if (out_lse != nullptr && !aligned(out_lse, 4)) return SA_ERR_INVALID_ARG;
-  if ((long long)n_tok * num_heads * 64 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;   // a wave per (token, head)
+  if ((long long)n_tok * num_heads * 256 >= kMaxGridThreads) return SA_ERR_UNSUPPORTED;   // 256 threads per (token, head)
   if (sa::launch_merge(part_o, part_lse, n_tok, num_splits, num_heads, head_dim, static_cast<uint16_t*>(out),
                        out_lse, stream) != hipSuccess)
     return SA_ERR_HIP;

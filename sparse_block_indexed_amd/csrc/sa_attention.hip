@@ -140,7 +140,8 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // Merge of the S partials of (token t, group g) into the output, by the
 // workgroup of the partition that arrived last: wave w computes the weights of
 // heads 4w .. 4w+3 (lane s holds partition s), then thread i accumulates dims
-// 4*((i % 16) + 16 j), j < 3, of head i / 16 over the partitions in order.
+// 4*((i % 16) + 16 j), j < 3, of head i / 16 in the merge kernel's order: four
+// quarter sums over consecutive partitions, added in quarter order.
 __device__ void merge_group(const AttnArgs& a, int t, int g, int S, float* s_w /* [16][64] */,
                             float* s_ml /* [16][2] */) {
   constexpr float kLog2e = 1.44269504088896340736f;
@@ -169,21 +170,40 @@ __device__ void merge_group(const AttnArgs& a, int t, int g, int S, float* s_w /
   const int head = g * kHeadsPerGroup + hl;
   const float* obase = a.part_o + ((size_t)t * S * kHeads + head) * kHeadDim + 4 * (tid & 15);
   const size_t sstride = (size_t)kHeads * kHeadDim;
-  f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int s0 = 0; s0 < S; s0 += 16) {
-    f32x4 v[16][3];
+  // the partitions in four consecutive quarters of R = ceil(S / 4): each
+  // quarter summed in partition order, then ((A0 + A1) + A2) + A3
+  const int R = (S + 3) / 4;
+  f32x4 qacc[4][3];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+  for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) qacc[qq][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    f32x4 v[8][3];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int j = 0; j < 3; ++j)
         v[u][j] = *reinterpret_cast<const f32x4*>(obase + (size_t)min(s0 + u, S - 1) * sstride + 64 * j);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < 8; ++u) {
       // a partition with no weight (empty, or past S) adds nothing
       const float wgt = s0 + u < S ? s_w[hl * 64 + min(s0 + u, 63)] : 0.f;
+      const int qs = (s0 + u) / R;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) acc[j] = wgt != 0.f ? acc[j] + v[u][j] * wgt : acc[j];
+      for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          qacc[qq][j] = (qs == qq && wgt != 0.f) ? qacc[qq][j] + v[u][j] * wgt : qacc[qq][j];
     }
+  }
+  f32x4 acc[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    acc[j] = qacc[0][j];
+    acc[j] = acc[j] + qacc[1][j];
+    acc[j] = acc[j] + qacc[2][j];
+    acc[j] = acc[j] + qacc[3][j];
   }
   const float M = s_ml[2 * hl], L = s_ml[2 * hl + 1];
   const float inv = L > 0.f ? 1.0f / L : 0.f;
