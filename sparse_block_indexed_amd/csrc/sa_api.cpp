@@ -188,7 +188,7 @@ static sa_status indexer_topk_impl(const void* q_idx, const void* k_idx_cache, b
   // dense GEMM and runs on MFMA; histories must fit the finalize-only select.
   a.use_gemm = n_rows >= 64 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
   // 16 .. 63 query rows per sequence (verify tokens x per-group queries): one
-  // MFMA pass scores 16 rows against each key, again for fused-select histories.
+  // MFMA pass scores 16 rows against each key, again for finalize-only histories.
   a.use_mfma16 = !a.use_gemm && n_rows >= 16 * pd.batch && a.max_hist_blocks <= sa::kFuseLimit;
   const int ngroups = a.use_mfma16 ? (n_rows + 15) / 16 : (n_rows + a.group_size - 1) / a.group_size;
   // Few long workgroups: about two per CU (the score kernel's occupancy), so

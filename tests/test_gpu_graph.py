@@ -121,7 +121,7 @@ def test_small_step_graph_replays_match_eager(num_splits, fp8_kv):
 
 
 def test_long_history_step_graph_replays_match_eager():
-    """Histories past the fused-select limit (zero + collect launches) under capture."""
+    """Histories past the finalize limit (candidate lists in the score pass + the select launch) under capture."""
     _say("graph long history")
     wl = I.make_workload(I.WorkloadSpec("long", batch=2, seq_lens=[200000, 30000], q_per_seq=2), seed=72,
                          device="cuda")

@@ -117,7 +117,7 @@ def test_grouped_fp8_keys_and_fp8_kv():
 
 def test_grouped_prefill_gemm_and_long_histories():
     """Many tokens per sequence (the MFMA score GEMM) and histories past the
-    fused-select limit (the collect launch), per group."""
+    finalize limit (candidate lists + the select launch), per group."""
     _say("grouped gemm + long")
     for spec, stride in ((I.WorkloadSpec("gg", batch=2, seq_lens=[5000, 9000], q_per_seq=70), 9),
                          (I.WorkloadSpec("gl", batch=2, seq_lens=[200000, 30000], q_per_seq=2), 1)):

@@ -195,31 +195,76 @@ def test_split_by_length_gives_short_lists_fewer_partitions():
 
 
 def test_all_scores_tied_takes_lowest_blocks():
-    """Index query of zeros: every score is 0, so the first 512 blocks win. The
-    history (5000 blocks) also overflows the candidate list and exercises the
-    select-over-all-scores path."""
+    """Index query of zeros: every score is 0, so the first 512 blocks win. In
+    the first call (histories up to 5000 blocks: finalize) the threshold bin
+    holds every score, more than the finalize's LDS tie buffer: the ordered
+    select over all scores. In the second (a 17,500-block history: candidate
+    lists) every chunk lists all of its keys, more than the select pass holds
+    in LDS: the ordered select over all scores as well."""
     _say("all tied")
-    spec = I.WorkloadSpec("tied", batch=2, seq_lens=[40001, 5000], q_per_seq=2)
-    wl = I.make_workload(spec, seed=21, device="cuda")
-    wl.q_idx.zero_()
+    for name, lens in (("tied", [40001, 5000]), ("tied_long", [140000, 5000])):
+        wl = I.make_workload(I.WorkloadSpec(name, batch=2, seq_lens=lens, q_per_seq=2), seed=21, device="cuda")
+        wl.q_idx.zero_()
+        sel, out, lse = run_sparse_layer(wl)
+        sel_h = sel.cpu().numpy()
+        for t in range(wl.n_tok):
+            cb = int(wl.q_pos[t]) // 8
+            assert sel_h[t].tolist() == list(range(min(512, cb))) + [-1] * (512 - min(512, cb)), f"{name} {t}"
+        _check_all(wl, sel, out, lse, range(wl.n_tok), what=name)
+
+
+def test_overflowing_candidate_list_is_reread():
+    """One chunk whose list would exceed the 512-entry cap: 30 one-token
+    sequences of 140,000 tokens (17,504-block tables) make the host score in
+    chunks of 1,024 blocks (30 x 18 chunks >= 512 workgroups), and the first
+    1,024 blocks of sequence 0 all carry the key 4*sign(q), the highest score
+    any key in [-4, 4] can reach. That chunk lists nothing (its edge is
+    "none"), the select pass re-reads it, and sequence 0 must select blocks
+    0 .. 511; every selection and output against the oracle."""
+    _say("overflowing candidate list")
+    spec = I.WorkloadSpec("overflow", batch=30, seq_lens=[140000] * 30, q_per_seq=1)
+    wl = I.make_workload(spec, seed=23, device="cuda")
+    t0 = int(np.flatnonzero(np.asarray(wl.q_seq) == 0)[0])
+    pages = torch.from_numpy(np.asarray(wl.page_table[0][:128], dtype=np.int64)).to(wl.k_idx_cache.device)
+    top = (4 * torch.sign(wl.q_idx[t0].float())).to(wl.k_idx_cache.dtype)
+    wl.k_idx_cache[pages] = top.view(1, 1, -1).expand(128, 8, -1)
     sel, out, lse = run_sparse_layer(wl)
     sel_h = sel.cpu().numpy()
+    assert sel_h[t0].tolist() == list(range(512))
+    # the list header of (row t0, chunk 0) in the workspace: count 0, edge "none"
+    # (headers follow the 256-byte aligned fp32 scores [n_tok][17,504], 18 per row)
+    from sparse_block_indexed_amd import ops
+    pt, sl, qs, qp = device_tables(wl)
+    ws = torch.zeros(ops.indexer_workspace_size(wl.n_tok, wl.max_pages_per_seq, 512), dtype=torch.uint8,
+                     device="cuda")
+    sel2 = ops.indexer_topk(wl.q_idx, wl.k_idx_cache, pt, sl, qs, qp, 512, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel2, sel)
+    mhb = wl.max_pages_per_seq * 8
+    meta_off = (wl.n_tok * mhb * 4 + 255) // 256 * 256
+    nck = (mhb + 1023) // 1024
+    head = ws[meta_off + 8 * (t0 * nck):meta_off + 8 * (t0 * nck + 2)].cpu().view(torch.int32).numpy().view(np.uint32)
+    assert head[0] == 0 and head[1] == 0xFFFFFFFF, head
+    assert head[3] != 0xFFFFFFFF and 0 < head[2] <= 512, head   # chunk 1 listed normally
+    ov = OracleView(wl)
     for t in range(wl.n_tok):
-        cb = int(wl.q_pos[t]) // 8
-        assert sel_h[t].tolist() == list(range(min(512, cb))) + [-1] * (512 - min(512, cb))
-    _check_all(wl, sel, out, lse, range(wl.n_tok), what="tied")
+        assert sel_h[t].tolist() == ov.selection(t).tolist(), f"token {t}"
+    _check_all(wl, sel, out, lse, range(wl.n_tok), what="overflow")
 
 
 def test_heavy_ties():
-    """Index inputs in {0, 1}: many blocks share the threshold score."""
+    """Index inputs in {0, 1}: many blocks share the threshold score. One call
+    of finalize rows, one with a 17,500-block row (candidate lists holding
+    long runs of tied keys, then the select pass)."""
     _say("heavy ties")
-    spec = I.WorkloadSpec("ties01", batch=3, seq_lens=[20000, 33000, 70000], q_per_seq=2, idx_lo=0, idx_hi=1)
-    wl = I.make_workload(spec, seed=22, device="cuda")
-    sel, out, lse = run_sparse_layer(wl)
-    ov = OracleView(wl)
-    sel_h = sel.cpu().numpy()
-    for t in range(wl.n_tok):
-        assert sel_h[t].tolist() == ov.selection(t).tolist(), f"token {t}"
+    for name, lens in (("ties01", [20000, 33000, 70000]), ("ties01_long", [140000, 33000])):
+        spec = I.WorkloadSpec(name, batch=len(lens), seq_lens=lens, q_per_seq=2, idx_lo=0, idx_hi=1)
+        wl = I.make_workload(spec, seed=22, device="cuda")
+        sel, out, lse = run_sparse_layer(wl)
+        ov = OracleView(wl)
+        sel_h = sel.cpu().numpy()
+        for t in range(wl.n_tok):
+            assert sel_h[t].tolist() == ov.selection(t).tolist(), f"{name} token {t}"
 
 
 def test_invalid_tokens_attend_nothing():
@@ -239,9 +284,9 @@ def test_invalid_tokens_attend_nothing():
 
 def test_invalid_positions_on_the_long_select_paths():
     """Tokens whose position is at or past their sequence's length but inside
-    the page table, so that their rows are located and scored: one on the fused
-    select (history above topk), one on the long-history select (score-pass
-    histogram, collect, candidate list; history above 16K blocks). Both select
+    the page table, so that their rows are located and scored: one on the
+    finalize (history above topk), one on the long-history select (candidate
+    lists in the score pass, then the select pass; history above 16K blocks). Both select
     nothing and attend nothing, in the sparse and the window layer; every other
     token matches the oracle."""
     _say("invalid positions, long select paths")
@@ -251,7 +296,7 @@ def test_invalid_positions_on_the_long_select_paths():
     assert wl.max_pages_per_seq * 64 > 139000
     t1 = [t for t in range(wl.n_tok) if int(wl.q_seq[t]) == 1]
     bad = t1[:2]
-    wl.q_pos[bad[0]] = 9000        # 1,125 historical blocks: fused select
+    wl.q_pos[bad[0]] = 9000        # 1,125 historical blocks: finalize
     wl.q_pos[bad[1]] = 139000      # 17,375 historical blocks: long-history select
     sel, out, lse = run_sparse_layer(wl)
     wout, wlse = run_swa(wl)
@@ -613,7 +658,7 @@ def test_sixteen_row_mfma_scorer_mixed_sequences(fp8_keys):
 
 
 def test_finalize_step_count_boundaries():
-    """The fused select runs the instantiation sized to the row's history: 2, 4,
+    """The finalize runs the instantiation sized to the row's history: 2, 4,
     8, 16 or 32 scores per thread of 512, so rows of 1,024 / 2,048 / 4,096 /
     8,192 blocks are the largest the first four hold. One row on either side of
     every boundary, all in one call, checked against the oracle."""
@@ -629,9 +674,10 @@ def test_finalize_step_count_boundaries():
 @pytest.mark.parametrize("q_per_seq", [3, 4])
 @pytest.mark.parametrize("fp8_keys", [False, True])
 def test_long_histories_with_three_and_four_tokens_per_sequence(q_per_seq, fp8_keys):
-    """Histories past the fused-select limit scored in runs of 3 or 4 tokens of
-    one sequence (the score pass then also builds each row's histogram), then
-    the collect and finalize launches; every selection against the oracle."""
+    """Histories past the finalize limit scored in runs of 3 or 4 tokens of one
+    sequence (the score pass then keeps each row's chunk and its histogram in
+    LDS and lists its candidates), then the select launch; every selection
+    against the oracle."""
     _say(f"long histories, {q_per_seq} tokens per sequence, fp8={fp8_keys}")
     from sparse_block_indexed_amd import ops
     wl = I.make_workload(I.WorkloadSpec("long_runs", batch=2, seq_lens=[140000, 20000], q_per_seq=q_per_seq),
@@ -648,12 +694,12 @@ def test_history_limits_of_the_select_paths():
     """Around the select paths' size limits, every selection checked against
     the oracle: a call whose longest history is exactly 16,384 blocks (scores
     held and selected by finalize alone), the same sequences plus one 8 tokens
-    longer (histograms, collect and candidates), and a context just past 2^17
-    blocks (no room for the LDS bitmaps: the ordered select over all scores)."""
+    longer (every row then takes the per-chunk candidate lists and the select
+    pass), and a context just past 2^17 blocks (513 chunks of 256 blocks)."""
     from sparse_block_indexed_amd import ops
-    cases = [("fused limit", [131072, 70000], 2),
-             ("collect path", [131072, 131080, 70000], 2),
-             ("past the bitmap limit", [1048576 + 64], 1)]
+    cases = [("finalize limit", [131072, 70000], 2),
+             ("candidate lists", [131072, 131080, 70000], 2),
+             ("past 2^17 blocks", [1048576 + 64], 1)]
     for name, lens, q in cases:
         _say(f"limits: {name}")
         wl = I.make_workload(I.WorkloadSpec(name, batch=len(lens), seq_lens=lens, q_per_seq=q), seed=51,
