@@ -688,8 +688,11 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(IndexerArgs a, int
 // once) and B = the 16 keys of the tile, loaded straight from the cache into
 // registers (lane (lq, lg): block lq of the tile). k-step i of lane group lg
 // covers dims 64*(i/2) + 16*lg + 8*(i%2) .. +8, so a lane's two k-steps of a
-// 64-dim slice are 16 contiguous dims (32 B of bf16, 16 B of fp8). The next
-// tile's keys are loaded while the current one is multiplied. Rows of another
+// 64-dim slice are 16 contiguous dims (32 B of bf16, 16 B of fp8), so one load
+// instruction reads half of each key's 128-byte lines and the next one the
+// other half: the key loads are cacheable (non-temporal loads fetched every
+// line twice from L2: 160 -> 151 us for the 128K batch's per-group indexer).
+// The next tile's keys are loaded while the current one is multiplied. Rows of another
 // sequence than the one being processed are handled in further passes.
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaTile = 16;
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(IndexerArgs a) {
         for (int j = 0; j < KL; ++j) {
           // bf16: slice j/2 (64 dims = 128 B), half j%2 of the lane's 32 B; fp8: slice j, the lane's 16 B
           const int off = kFp8 ? 64 * j + 16 * lg : 128 * (j >> 1) + 32 * lg + 16 * (j & 1);
-          kb[j] = load16_stream(p + off);
+          kb[j] = load16(p + off);   // cacheable: the other half of each 128-byte line comes from L1
         }
       };
       const int ntiles = (whi - wlo + kMfmaTile - 1) / kMfmaTile;
