@@ -236,7 +236,7 @@ int sa_resolve_num_splits(int n_tok, int max_blocks_per_token, int num_splits);
  *              lse = -inf attended nothing and its part_o may hold anything
  * merge_counters  device uint32 [n_tok][4] or NULL; used when S > 1 and out is
  *              non-NULL: the last partition of each (token, group) to finish
- *              merges the S partials in the same launch (partition order, the
+ *              merges the S partials in the same launch (the order and
  *              arithmetic of sa_merge, so the result is the same bit for bit).
  *              They must be zero before the first call that uses them, and
  *              every such call leaves them zero (allocate and zero once; a
@@ -317,11 +317,15 @@ sa_status sa_swa_decode_fp8kv(const void* q, const void* k_cache_fp8, const void
  * With M = max_s lse_s: O = sum_s e^(lse_s - M) O_s / sum_s e^(lse_s - M),
  * lse = M + ln sum_s e^(lse_s - M). Partitions with lse = -inf carry no weight
  * and their part_o is not used (it may hold anything, NaN included); if all are
- * empty the output is 0 and lse = -inf.
+ * empty the output is 0 and lse = -inf. The sum runs in a fixed order (four
+ * consecutive quarters of the partitions, each in partition order, then the
+ * quarters in order), so the result is deterministic.
  * part_o device fp32 [n_tok][num_splits][num_heads][head_dim]; part_lse
  * [n_tok][num_splits][num_heads]; out device bf16 [n_tok][num_heads][head_dim];
  * out_lse fp32 [n_tok][num_heads] or NULL. head_dim must be a multiple of 4
- * and at most 1024; num_heads at most 1024; num_splits 1 .. SA_MAX_SPLITS.
+ * and at most 1024; num_heads at most 1024; num_splits 1 .. SA_MAX_SPLITS;
+ * n_tok * num_heads * 256 below 2^32 (one 256-thread workgroup per (token,
+ * head)), else SA_ERR_UNSUPPORTED.
  */
 sa_status sa_merge(const float* part_o, const float* part_lse, int n_tok, int num_splits,
                    int num_heads, int head_dim, void* out, float* out_lse, hipStream_t stream);

@@ -1,9 +1,10 @@
 // sa_indexer_topk_noalloc: the indexer entry point for callers that cannot
 // allocate device memory (code under HIP graph capture, tight serving loops,
-// harnesses that forbid hipMalloc). The indexer's workspace (score rows,
-// histograms, candidate lists) lives in a file-scope device array of fixed
-// size instead of a caller buffer; every other argument and the result are
-// those of sa_indexer_topk, whose kernels it runs.
+// harnesses that forbid hipMalloc). The indexer's workspace (score rows, and
+// for long histories the candidate-list headers and lists) lives in a
+// file-scope device array of fixed size instead of a caller buffer; every
+// other argument and the result are those of sa_indexer_topk, whose kernels
+// it runs.
 //
 // The array exists once per GPU the library runs on and is held until the
 // process ends. Its device address is looked up once per device, with that

@@ -112,8 +112,8 @@ int main() {
          SA_ERR_INVALID_ARG, "sparse misaligned K");
   expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 1 << 22, 512, 0.1f, 1, nullptr, nullptr, nullptr, P, nullptr, nullptr),
          SA_ERR_UNSUPPORTED, "sparse grid limit");
-  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 1 << 20, 512, 0.1f, 2, PF, PF, nullptr, P, nullptr, nullptr),
-         SA_ERR_UNSUPPORTED, "sparse merge grid limit");
+  expect(sa_sparse_decode(P, P, P, d, PI, PI, PI, 1 << 18, 512, 0.1f, 2, PF, PF, nullptr, P, nullptr, nullptr),
+         SA_ERR_UNSUPPORTED, "sparse merge grid limit");   // 2^18 tokens x 64 heads x 256 threads
   expect(sa_sparse_decode_fp8kv(P, P, P, 0.f, 1.f, d, PI, PI, PI, 4, 512, sc, 1, nullptr, nullptr, nullptr, P, nullptr,
                                 nullptr),
          SA_ERR_INVALID_ARG, "fp8 KV zero scale");
@@ -141,7 +141,7 @@ int main() {
   expect(sa_merge(PF, PF, 2, 0, 64, 192, P, nullptr, nullptr), SA_ERR_INVALID_ARG, "merge 0 splits");
   expect(sa_merge(PF, PF, 2, 65, 64, 192, P, nullptr, nullptr), SA_ERR_UNSUPPORTED, "merge 65 splits");
   expect(sa_merge(PF, PF, 2, 4, 64, 190, P, nullptr, nullptr), SA_ERR_UNSUPPORTED, "merge head dim 190");
-  expect(sa_merge(PF, PF, 1 << 20, 2, 64, 192, P, nullptr, nullptr), SA_ERR_UNSUPPORTED, "merge grid limit");
+  expect(sa_merge(PF, PF, 1 << 18, 2, 64, 192, P, nullptr, nullptr), SA_ERR_UNSUPPORTED, "merge grid limit");
 
   // split policy and status names
   expect(sa_resolve_num_splits(1, 513, SA_SPLITS_FILL_GPU), 32, "fill the GPU: one 8K token, 32 partitions");

@@ -245,9 +245,9 @@ def test_grid_limits_are_refused(lib):
     f = lib.sa_sparse_decode
     assert f(P, P, P, d, P, P, P, 1 << 22, 512, ctypes.c_float(0.1), 1, None, None, None, P, None, None) \
         == ops.SA_ERR_UNSUPPORTED                                               # 2^22 tokens x 4 groups x 256
-    assert f(P, P, P, d, P, P, P, 1 << 20, 512, ctypes.c_float(0.1), 2, P, P, None, P, None, None) \
-        == ops.SA_ERR_UNSUPPORTED                                               # the merge: 2^20 x 64 heads x 64
-    assert lib.sa_merge(P, P, 1 << 20, 2, 64, 192, P, None, None) == ops.SA_ERR_UNSUPPORTED
+    assert f(P, P, P, d, P, P, P, 1 << 18, 512, ctypes.c_float(0.1), 2, P, P, None, P, None, None) \
+        == ops.SA_ERR_UNSUPPORTED                                               # the merge: 2^18 x 64 heads x 256
+    assert lib.sa_merge(P, P, 1 << 18, 2, 64, 192, P, None, None) == ops.SA_ERR_UNSUPPORTED
 
 
 def test_swa_and_merge_validation(lib):
