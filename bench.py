@@ -190,6 +190,7 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
     except Exception:
         threads = 1
     done, t_cpu = 0, 0.0
+    t_sel, t_att = 0.0, 0.0   # the two parts of the oracle's per-token work
     seqs_done = 0
     refs = []
     dev = wl.k_cache.device
@@ -231,20 +232,26 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
         t0 = time.perf_counter()
         for j, t in enumerate(toks):
             p = int(wl.q_pos[t])
+            ta = time.perf_counter()
             if window is not None:
                 sel = None
+                tb = time.perf_counter()
                 o, l = O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.window_positions(p, window),
                                           SCALE, fp8_scales=fp8_scales)
             elif q_groups is None:
                 keys = O.index_keys(kidx, np.arange(npg), p // 8, fp8=kidx_fp8 is not None)
                 sel = O.indexer_topk_token(O.bf16_to_f64(qib[j]), keys, 512)
+                tb = time.perf_counter()
                 o, l = O.attend_positions(O.bf16_to_f64(qb[j]), kc, vc, compact, O.sparse_token_positions(sel, p),
                                           SCALE, fp8_scales=fp8_scales)
             else:
                 keys = O.index_keys(kidx, np.arange(npg), p // 8, fp8=kidx_fp8 is not None)
                 sel = np.stack([O.indexer_topk_token(O.bf16_to_f64(qib[j][g]), keys, 512) for g in range(4)])
+                tb = time.perf_counter()
                 o, l = O.sparse_attention_token_grouped(qb[j], kc, vc, compact, sel, p, SCALE,
                                                         fp8_scales=fp8_scales)
+            t_sel += tb - ta
+            t_att += time.perf_counter() - tb
             refs.append((t, sel, o, l))
             done += 1
             if time.perf_counter() - t0 + t_cpu >= budget_s:
@@ -253,9 +260,16 @@ def cpu_baseline(wl, sel_host, window=None, budget_s: float = 20.0, max_tokens: 
         seqs_done += 1
         if t_cpu >= budget_s or done >= max_tokens:
             break
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return ({"value": done / t_cpu, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
              "sample": f"{done} query tokens ({seqs_done} sequences) of the {wl.spec.name} workload, fp64 numpy "
-                       f"oracle, {t_cpu:.1f} s of CPU time, host copies excluded"}, refs)
+                       f"oracle, {t_cpu:.1f} s of CPU time, host copies excluded",
+             "host": {"os_cpu_count": os.cpu_count(), "affinity_cores": affinity, "blas_threads": threads},
+             "seconds_per_token": {"indexer_topk": t_sel / max(done, 1), "attention": t_att / max(done, 1)}},
+            refs)
 
 
 MAX_ABS, REL_RMS, LSE_ABS = 2e-2, 5e-3, 1e-3

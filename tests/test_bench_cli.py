@@ -57,3 +57,37 @@ def test_parity_check_of_timed_buffers():
     assert not bench.parity_check(refs, sel_host, bad_out, lse)["pass"]
     window_refs = [(t, None, o, l) for t, _, o, l in refs]
     assert bench.parity_check(window_refs, None, out, lse)["selection"] is None
+
+
+def test_cpu_baseline_leg_on_a_small_workload():
+    """The bench's oracle leg on a small CPU workload: it reports the host's core
+    counts, its BLAS threads and the per-token time of its two parts, and the
+    results it returns for the parity check pass that check against the oracle's
+    own selections and outputs (as the timed buffers would hold them)."""
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    try:
+        import bench
+        from gpu_helpers import OracleView
+    finally:
+        sys.path.pop(0)
+        sys.path.pop(0)
+    from sparse_block_indexed_amd import inputs as I
+    wl = I.make_workload(I.WorkloadSpec("tiny", batch=2, seq_lens=[5000, 700], q_per_seq=2), seed=3, device="cpu")
+    ov = OracleView(wl)
+    sel_host = np.stack([ov.selection(t) for t in range(wl.n_tok)]).astype(np.int32)
+    base, refs = bench.cpu_baseline(wl, sel_host, budget_s=30.0, max_tokens=4)
+    assert base["kind"] == "oracle" and base["value"] > 0 and len(refs) == wl.n_tok
+    assert base["host"]["os_cpu_count"] == os.cpu_count() and base["host"]["blas_threads"] >= 1
+    assert base["seconds_per_token"]["indexer_topk"] > 0 and base["seconds_per_token"]["attention"] > 0
+    for t, sel, _, _ in refs:
+        assert sel.tolist() == sel_host[t].tolist()
+    out = torch.zeros((wl.n_tok, 64, 192), dtype=torch.bfloat16)
+    lse = torch.zeros((wl.n_tok, 64), dtype=torch.float32)
+    for t, _, o, l in refs:
+        out[t] = torch.tensor(o, dtype=torch.float32).to(torch.bfloat16)
+        lse[t] = torch.tensor(l, dtype=torch.float32)
+    assert bench.parity_check(refs, sel_host, out, lse)["pass"]
