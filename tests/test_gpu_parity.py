@@ -80,6 +80,41 @@ def test_small_topk_values(topk):
     _check_all(wl, sel, out, lse, range(wl.n_tok), topk=topk, what=f"topk={topk}")
 
 
+@pytest.mark.parametrize("topk", [1, 7, 100, 511])
+def test_small_topk_values_on_long_histories(topk):
+    """The candidate-list path (histories past 16,384 blocks, whose per-chunk
+    budgets follow k) with small k, next to a short row of the same call."""
+    _say(f"long histories, topk={topk}")
+    spec = I.WorkloadSpec("long_topk", batch=3, seq_lens=[140000, 131080, 3000], q_per_seq=2)
+    wl = I.make_workload(spec, seed=17, device="cuda")
+    sel, out, lse = run_sparse_layer(wl, topk=topk)
+    _check_all(wl, sel, out, lse, range(wl.n_tok), topk=topk, what=f"long topk={topk}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_calls(seed):
+    """Seeded random calls: 1-5 sequences of random lengths (half of them with
+    one history past 16,384 blocks, so that the candidate-list path runs), 1-4
+    query tokens per sequence, k in {1, 16, 100, 512}, index values in [-4, 4],
+    {0, 1} or [-1, 1] (ties), and any split setting; every token's selection and
+    output against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    batch = int(rng.integers(1, 6))
+    lens = [int(rng.integers(1, 20000)) for _ in range(batch)]
+    if rng.random() < 0.5:
+        lens[int(rng.integers(0, batch))] = int(rng.integers(131080, 180000))
+    q = int(rng.integers(1, 5))
+    topk = int(rng.choice([1, 16, 100, 512]))
+    lo, hi = [(-4, 4), (0, 1), (-1, 1)][int(rng.integers(0, 3))]
+    num_splits = int(rng.choice([0, -1, 1, 3]))
+    what = f"random {seed}: lens {lens}, q {q}, k {topk}, idx [{lo}, {hi}], splits {num_splits}"
+    _say(what)
+    spec = I.WorkloadSpec(f"random{seed}", batch=batch, seq_lens=lens, q_per_seq=q, idx_lo=lo, idx_hi=hi)
+    wl = I.make_workload(spec, seed=300 + seed, device="cuda")
+    sel, out, lse = run_sparse_layer(wl, topk=topk, num_splits=num_splits)
+    _check_all(wl, sel, out, lse, range(wl.n_tok), topk=topk, what=what)
+
+
 # The five workloads run at full size in the launch configuration the benchmark
 # times (partition count following the call's size).
 
