@@ -139,3 +139,26 @@ def test_grouped_mtp_verify_fp8_keys_takes_the_16_row_scorer():
     rng = np.random.default_rng(2)
     toks = sorted(rng.choice(wl.n_tok, size=32, replace=False).tolist())
     _check(wl, qg, sel, out, lse, toks, toks[:4], kidx_fp8=codes, what="grouped 128K fp8 keys")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_grouped_calls(seed):
+    """Seeded random per-group calls: 1-4 sequences of random lengths (half of
+    them with one history past 16,384 blocks), 1-4 query tokens each (1-3 use
+    the per-token scorer's runs, 4 the 16-row MFMA scorer when every sequence
+    has 4), random per-group index queries and any split setting; every (token,
+    group) selection and every output against the oracle."""
+    rng = np.random.default_rng(3000 + seed)
+    batch = int(rng.integers(1, 5))
+    lens = [int(rng.integers(1, 20000)) for _ in range(batch)]
+    if rng.random() < 0.5:
+        lens[int(rng.integers(0, batch))] = int(rng.integers(131080, 160000))
+    q = int(rng.integers(1, 5))
+    num_splits = int(rng.choice([0, -1, 1, 3]))
+    what = f"random grouped {seed}: lens {lens}, q {q}, splits {num_splits}"
+    _say(what)
+    wl = I.make_workload(I.WorkloadSpec(f"rgrp{seed}", batch=batch, seq_lens=lens, q_per_seq=q), seed=500 + seed,
+                         device="cuda")
+    qg = I.grouped_index_queries(wl.n_tok, seed=600 + seed, device="cuda")
+    sel, out, lse = _run(wl, qg, num_splits=num_splits)
+    _check(wl, qg, sel, out, lse, range(wl.n_tok), range(wl.n_tok), what=what)

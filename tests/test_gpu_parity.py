@@ -72,6 +72,29 @@ def test_small_mixed_swa(window, num_splits):
                          np.stack([r[1] for r in refs]), f"swa W={window}")
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_window_calls(seed):
+    """Seeded random window calls: 1-6 sequences of random lengths, 1-4 query
+    tokens each, a window in 1 .. 4096 and any split setting; every token
+    against the oracle."""
+    from gpu_helpers import run_swa
+    rng = np.random.default_rng(2000 + seed)
+    batch = int(rng.integers(1, 7))
+    lens = [int(rng.integers(1, 40000)) for _ in range(batch)]
+    q = int(rng.integers(1, 5))
+    window = int(rng.choice([1, int(rng.integers(2, 600)), 512, int(rng.integers(600, 4097))]))
+    num_splits = int(rng.choice([0, -1, 1, 2, 5]))
+    what = f"random window {seed}: lens {lens}, q {q}, window {window}, splits {num_splits}"
+    _say(what)
+    wl = I.make_workload(I.WorkloadSpec(f"rwin{seed}", batch=batch, seq_lens=lens, q_per_seq=q), seed=400 + seed,
+                         device="cuda")
+    out, lse = run_swa(wl, window=window, num_splits=num_splits)
+    ov = OracleView(wl)
+    refs = [ov.swa(t, window) for t in range(wl.n_tok)]
+    assert_close_outputs(bf16_to_np(out), lse.cpu().numpy(), np.stack([r[0] for r in refs]),
+                         np.stack([r[1] for r in refs]), what)
+
+
 @pytest.mark.parametrize("topk", [1, 7, 100, 511])
 def test_small_topk_values(topk):
     _say(f"topk={topk}")
