@@ -158,10 +158,10 @@ def write_pmc_record(args):
             total += b
         phases[phase] = {"kernels": kern, "bytes_per_call": int(round(total))}
     rec = {"workload": args.workload,
-           "commands": {c: f"rocprofv3 --pmc {c} -d gpurun_out/pmc/{args.workload}_{c} -o bench --output-format csv "
+           "commands": {c: f"rocprofv3 --pmc {c} -d pmc/{args.workload}_{c} -o bench --output-format csv "
                            f"-- python3 bench.py --workload {args.workload} --eager --steps 3 --warmup 1 "
                            f"--cold-steps 0 --no-cpu-baseline" for c in dirs},
-           "copy_calibration_command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d gpurun_out/pmc/copy_<counter> "
+           "copy_calibration_command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d pmc/copy_<counter> "
                                        "-o copy --output-format csv -- python3 bench.py --copy-calibration",
            "copy_calibration": cal, "phases": phases,
            "source_sha256_16": {n: source_hash(n) for n in ("sa_indexer.hip", "sa_attention.hip", "sa_merge.hip")}}
