@@ -1268,6 +1268,53 @@ __device__ uint32_t radix_kth_range(KeyAt key_at, int m, uint32_t k, uint32_t* h
   return base;
 }
 
+// The same k-th largest when the caller already knows the keys' range
+// [kmin, kmax] (no pass over the keys to find it): the histogram pass also
+// keeps each bin's smallest and largest key, so the single-value check after a
+// level is two reads instead of another pass.
+template <int NT, typename KeyAt>
+__device__ __forceinline__ uint32_t radix_kth_span(KeyAt key_at, int m, uint32_t k, uint32_t kmin, uint32_t kmax,
+                                                   uint32_t* h, uint32_t* hmin, uint32_t* hmax, uint32_t* tmp,
+                                                   uint32_t* res, uint32_t* count_gt) {
+  uint32_t base = kmin;                                     // window [base, base + 2^width)
+  int width = kmax > kmin ? 32 - __clz(kmax - kmin) : 0;    // kmax - kmin < 2^width
+  uint32_t above = 0;
+  while (width > 0) {   // (uniform)
+    const int sh = max(0, width - 11);
+    for (int i = threadIdx.x; i < kHistBins; i += NT) {
+      h[i] = 0u;
+      hmin[i] = 0xFFFFFFFFu;
+      hmax[i] = 0u;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < m; i += NT) {
+      const uint32_t x = key_at(i);
+      const uint32_t d = x - base;   // (wraps to a large value below the window)
+      if (x >= base && (width >= 32 || d < (1u << width))) {
+        const uint32_t b = d >> sh;
+        atomicAdd(&h[b], 1u);
+        atomicMin(&hmin[b], x);
+        atomicMax(&hmax[b], x);
+      }
+    }
+    __syncthreads();
+    select_bin<NT>(h, kHistBins, k - above, tmp, res);
+    const uint32_t b = res[0], cnt = res[1];
+    const uint32_t bmin = hmin[b], bmax = hmax[b];
+    __syncthreads();   // every thread has read res and the bin's extremes
+    base += b << sh;
+    above += cnt;
+    width = sh;
+    if (width == 0) break;
+    if (bmin == bmax) {   // (uniform) one value: it is the k-th largest
+      base = bmin;
+      break;
+    }
+  }
+  *count_gt = above;
+  return base;
+}
+
 // ---------------------------------------------------------------------------
 // 4. select (after the per-token scorer)
 // ---------------------------------------------------------------------------
@@ -1294,6 +1341,9 @@ struct alignas(16) SelectLds {
   uint32_t fkey[kSelCap];   // F, when some chunk had to be re-read
   uint32_t fid[kSelCap];
   uint32_t h[kHistBins];
+  uint32_t hmin[kHistBins];           // smallest and largest key of each bin (tau_U)
+  uint32_t hmax[kHistBins];
+  uint32_t krange[2];                 // smallest and largest key of U
   uint32_t off[kSelMaxChunks + 1];    // first entry of each chunk's list in U
   uint32_t foff[kSelMaxChunks + 1];   // first entry of each chunk in F (its count, before the scan)
   uint32_t edge[kSelMaxChunks];
@@ -1365,6 +1415,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
       s.edge[c] = mv[r].y;
     }
   }
+  if (threadIdx.x == 0) {
+    s.krange[0] = 0xFFFFFFFFu;
+    s.krange[1] = 0u;
+  }
   __syncthreads();
   chunk_scan(s.off, nck, s.tmp);
   const uint32_t m_u = s.off[nck];
@@ -1374,7 +1428,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   }
   // 2. U in chunk order: thread i copies the lists of chunks i and i + 512,
   // 16 entries (eight 16-byte loads, all issued before any is waited for) at a
-  // time; the lists start 16-byte aligned (capacities are multiples of 64)
+  // time; the lists start 16-byte aligned (capacities are multiples of 64).
+  // The copy also finds U's key range (for tau_U).
+  uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
   for (int c = threadIdx.x; c < nck; c += kSelThreads) {
     const uint32_t o = s.off[c], n = s.off[c + 1] - o;
     const uint4* src = reinterpret_cast<const uint4*>(lists + (size_t)c * a.cand_cap);
@@ -1388,13 +1444,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
         if (j < n) {
           s.key[o + j] = e[r].x;
           s.id[o + j] = e[r].y;
+          lmin = min(lmin, e[r].x);
+          lmax = max(lmax, e[r].x);
         }
         if (j + 1 < n) {
           s.key[o + j + 1] = e[r].z;
           s.id[o + j + 1] = e[r].w;
+          lmin = min(lmin, e[r].z);
+          lmax = max(lmax, e[r].z);
         }
       }
     }
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    lmin = min(lmin, (uint32_t)__shfl_xor((int)lmin, d));
+    lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, d));
+  }
+  if (lane == 0) {
+    atomicMin(&s.krange[0], lmin);
+    atomicMax(&s.krange[1], lmax);
   }
   __syncthreads();
   // 3. tau_U (every key, 0, when fewer than k are listed)
@@ -1402,8 +1471,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   uint32_t tau = 0;
   if (m_u >= (uint32_t)k) {
     const uint32_t* keys = s.key;
-    tau = radix_kth_range<kSelThreads>([keys](int i) { return keys[i]; }, (int)m_u, (uint32_t)k, s.h, s.tmp, s.res,
-                                        &gt);
+    tau = radix_kth_span<kSelThreads>([keys](int i) { return keys[i]; }, (int)m_u, (uint32_t)k, s.krange[0],
+                                       s.krange[1], s.h, s.hmin, s.hmax, s.tmp, s.res, &gt);
   }
   // 4. chunks that may hold unlisted keys >= tau_U
   bool mine = m_u < (uint32_t)k;
