@@ -231,3 +231,32 @@ def test_fp8kv_constant_v_closed_form():
     for t in range(wl.n_tok):
         ro, rl = ov.sparse(t, sel[t].cpu().numpy())
         assert np.abs(lse[t].cpu().numpy() - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fp8kv_random_calls(seed):
+    """Seeded random one-byte K/V calls: 1-5 sequences of random lengths (half
+    of them with one history past 16,384 blocks), 1-4 query tokens each, k in
+    {1, 100, 512}, any split setting, then the window layer over the same caches
+    with a random window; every token against the oracle's own decoding."""
+    rng = np.random.default_rng(4000 + seed)
+    batch = int(rng.integers(1, 6))
+    lens = [int(rng.integers(1, 20000)) for _ in range(batch)]
+    if rng.random() < 0.5:
+        lens[int(rng.integers(0, batch))] = int(rng.integers(131080, 160000))
+    q = int(rng.integers(1, 5))
+    topk = int(rng.choice([1, 100, 512]))
+    num_splits = int(rng.choice([0, -1, 1, 3]))
+    window = int(rng.choice([1, 512, int(rng.integers(2, 4097))]))
+    what = f"fp8kv random {seed}: lens {lens}, q {q}, k {topk}, splits {num_splits}, window {window}"
+    _say(what)
+    wl = I.make_workload(I.WorkloadSpec(f"f8r{seed}", batch=batch, seq_lens=lens, q_per_seq=q), seed=700 + seed,
+                         device="cuda")
+    kv = _quantize(wl)
+    sel, out, lse = run_sparse_layer(wl, topk=topk, num_splits=num_splits, kv_fp8=kv)
+    _check_sparse(wl, kv, sel, out, lse, range(wl.n_tok), topk=topk, what=what)
+    wout, wlse = run_swa(wl, window=window, num_splits=num_splits, kv_fp8=kv)
+    ov = OracleView(wl, kv_fp8=kv)
+    refs = [ov.swa(t, window) for t in range(wl.n_tok)]
+    assert_close_outputs(bf16_to_np(wout), wlse.cpu().numpy(), np.stack([r[0] for r in refs]),
+                         np.stack([r[1] for r in refs]), what + " (window)")
