@@ -60,8 +60,15 @@ def pmc_file(workload: str) -> str:
 
 
 def source_hash(name: str) -> str:
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and white space are left out,
+    so that a counter record stays valid across edits that change no code."""
+    import re
+    with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def counter_traffic(workload: str, phase: str):

@@ -34,8 +34,8 @@
 // Split calls (S > 1) write one partial result per partition. With kMerge the
 // partitions of a (token, group) count their arrivals on an integer counter
 // once their partial is visible device-wide; the last to arrive resets the
-// counter and merges the S partials in partition order with exactly the
-// arithmetic of the merge kernel, so no second launch is needed.
+// counter and merges the S partials in the merge kernel's order and with its
+// exact arithmetic, so no second launch is needed.
 
 #include <type_traits>
 

@@ -91,3 +91,24 @@ def test_cpu_baseline_leg_on_a_small_workload():
         out[t] = torch.tensor(o, dtype=torch.float32).to(torch.bfloat16)
         lse[t] = torch.tensor(l, dtype=torch.float32)
     assert bench.parity_check(refs, sel_host, out, lse)["pass"]
+
+
+def test_counter_records_follow_code_not_comments(tmp_path):
+    """A counter record's source hash ignores comments and spacing, and changes
+    with the code."""
+    sys.path.insert(0, ROOT)
+    try:
+        import bench
+    finally:
+        sys.path.pop(0)
+    saved = bench.CSRC
+    bench.CSRC = str(tmp_path)
+    try:
+        def h(text):
+            (tmp_path / "k.hip").write_text(text)
+            return bench.source_hash("k.hip")
+        base = h("int f(int x) {\n  return x + 1;   // add one\n}\n")
+        assert h("/* header */\nint f(int x) {\n    return x + 1;\n}\n") == base
+        assert h("int f(int x) {\n  return x + 2;   // add one\n}\n") != base
+    finally:
+        bench.CSRC = saved
