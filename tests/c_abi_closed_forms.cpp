@@ -154,6 +154,19 @@ int main() {
     }
     check(ok, "top-16 by block id, by negated block id, empty history, invalid sequence");
   }
+  {
+    // the entry point for callers that cannot allocate: the same ids, twice in a row
+    int32_t* d_sel2 = nullptr;
+    hip_ok(hipMalloc((void**)&d_sel2, sizeof(int32_t) * n_tok * topk), "hipMalloc sel2");
+    bool ok = true;
+    for (int rep = 0; rep < 2; ++rep) {
+      ok &= sa_indexer_topk_noalloc(d_qidx, d_kidx, pd, d_qs, d_qp, n_tok, topk, d_sel2, stream) == SA_OK;
+      hip_ok(hipStreamSynchronize(stream), "sync noalloc indexer");
+      ok &= to_host(d_sel2, (size_t)n_tok * topk) == sel;
+    }
+    check(ok, "sa_indexer_topk_noalloc gives sa_indexer_topk's ids");
+    hipFree(d_sel2);
+  }
 
   // ---- attention with a V constant per group ---------------------------
   float *d_part_o = nullptr, *d_part_lse = nullptr, *d_lse = nullptr;
