@@ -24,29 +24,29 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _run(wl, qg, num_splits=0, kidx=None, kv=None):
+def _run(wl, qg, num_splits=0, kidx=None, kv=None, topk=512):
     from sparse_block_indexed_amd import ops
     pt, sl, qs, qp = device_tables(wl)
-    sel = ops.indexer_topk(qg, wl.k_idx_cache if kidx is None else kidx, pt, sl, qs, qp, 512)
+    sel = ops.indexer_topk(qg, wl.k_idx_cache if kidx is None else kidx, pt, sl, qs, qp, topk)
     kc, vc, kw = (wl.k_cache, wl.v_cache, {}) if kv is None else (kv[0], kv[1], dict(k_scale=kv[2], v_scale=kv[3]))
     out, lse = ops.sparse_decode(wl.q, kc, vc, pt, sl, qs, qp, sel, SCALE, num_splits=num_splits, **kw)
     torch.cuda.synchronize()
     return sel, out, lse
 
 
-def _check(wl, qg, sel, out, lse, sel_tokens, attn_tokens, kidx_fp8=None, kv=None, what=""):
-    assert sel.shape == (wl.n_tok, 4, 512)
+def _check(wl, qg, sel, out, lse, sel_tokens, attn_tokens, kidx_fp8=None, kv=None, what="", topk=512):
+    assert sel.shape == (wl.n_tok, 4, topk)
     ov = OracleView(wl, kidx_fp8=kidx_fp8, kv_fp8=kv)
     sel_h = sel.cpu().numpy()
     refs = {}
     for t in sel_tokens:
-        ref = ov.selection_grouped(t, qg)
+        ref = ov.selection_grouped(t, qg, topk)
         for g in range(4):
             assert sel_h[t, g].tolist() == ref[g].tolist(), f"{what}: token {t} group {g} selection differs"
         refs[t] = ref
     outs, ros, lses, rls = [], [], [], []
     for t in attn_tokens:
-        ro, rl = ov.sparse_grouped(t, refs[t] if t in refs else ov.selection_grouped(t, qg))
+        ro, rl = ov.sparse_grouped(t, refs[t] if t in refs else ov.selection_grouped(t, qg, topk))
         outs.append(bf16_to_np(out[t]))
         lses.append(lse[t].cpu().numpy())
         ros.append(ro)
@@ -147,7 +147,7 @@ def test_random_grouped_calls(seed):
     them with one history past 16,384 blocks), 1-4 query tokens each (1-3 use
     the per-token scorer's runs, 4 the 16-row MFMA scorer when every sequence
     has 4), random per-group index queries and any split setting; every (token,
-    group) selection and every output against the oracle."""
+    group) selection and every output against the oracle; k in {1, 100, 512}."""
     rng = np.random.default_rng(3000 + seed)
     batch = int(rng.integers(1, 5))
     lens = [int(rng.integers(1, 20000)) for _ in range(batch)]
@@ -155,10 +155,11 @@ def test_random_grouped_calls(seed):
         lens[int(rng.integers(0, batch))] = int(rng.integers(131080, 160000))
     q = int(rng.integers(1, 5))
     num_splits = int(rng.choice([0, -1, 1, 3]))
-    what = f"random grouped {seed}: lens {lens}, q {q}, splits {num_splits}"
+    topk = int(rng.choice([1, 100, 512]))
+    what = f"random grouped {seed}: lens {lens}, q {q}, k {topk}, splits {num_splits}"
     _say(what)
     wl = I.make_workload(I.WorkloadSpec(f"rgrp{seed}", batch=batch, seq_lens=lens, q_per_seq=q), seed=500 + seed,
                          device="cuda")
     qg = I.grouped_index_queries(wl.n_tok, seed=600 + seed, device="cuda")
-    sel, out, lse = _run(wl, qg, num_splits=num_splits)
-    _check(wl, qg, sel, out, lse, range(wl.n_tok), range(wl.n_tok), what=what)
+    sel, out, lse = _run(wl, qg, num_splits=num_splits, topk=topk)
+    _check(wl, qg, sel, out, lse, range(wl.n_tok), range(wl.n_tok), what=what, topk=topk)

@@ -445,6 +445,42 @@ def test_unreadable_pages_rank_last_and_are_skipped(q_per_seq, fp8_keys):
     assert_close_outputs(np.stack(outs), np.stack(lses), np.stack(refs), np.stack(rlses), "unreadable pages")
 
 
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_unreadable_pages_in_the_window_are_skipped(num_splits):
+    """Window layer: page-table entries outside [0, num_pages) (-1, and past the
+    cache) on pages inside the window (never the query's own page): the
+    tokens of those pages are skipped, the rest of the window attended."""
+    _say(f"unreadable window pages S={num_splits}")
+    from sparse_block_indexed_amd import ops
+    wl = I.make_workload(I.WorkloadSpec("bad_win", batch=2, seq_lens=[3000, 9000], q_per_seq=2), seed=62,
+                         device="cuda")
+    window = 2048
+    ov = OracleView(wl)   # reads K/V through the intact table
+    bad = {}
+    pt_bad = wl.page_table.copy()
+    for b in range(wl.batch):
+        last = (int(wl.seq_lens[b]) - 2) // 64   # the page of the sequence's first query token
+        bad[b] = [last - 2, last - 5]
+        pt_bad[b, last - 2] = -1
+        pt_bad[b, last - 5] = wl.num_pages + 3
+    _, sl, qs, qp = device_tables(wl)
+    pt = torch.as_tensor(pt_bad, dtype=torch.int32, device="cuda")
+    out, lse = ops.swa_decode(wl.q, wl.k_cache, wl.v_cache, pt, sl, qs, qp, window, SCALE, num_splits=num_splits)
+    torch.cuda.synchronize()
+    outs, refs, lses, rlses = [], [], [], []
+    for t in range(wl.n_tok):
+        b, p = int(wl.q_seq[t]), int(wl.q_pos[t])
+        assert all(lp != p // 64 for lp in bad[b])
+        pos = O.window_positions(p, window)
+        pos = pos[~np.isin(pos // 64, bad[b])]
+        ro, rl = ov.attention(t, pos)
+        outs.append(bf16_to_np(out[t]))
+        lses.append(lse[t].cpu().numpy())
+        refs.append(ro)
+        rlses.append(rl)
+    assert_close_outputs(np.stack(outs), np.stack(lses), np.stack(refs), np.stack(rlses), "unreadable window pages")
+
+
 def test_deterministic_and_batch_invariant():
     _say("determinism")
     wl = I.named_workload("decode_8k_b1", device="cuda", seed=31)
